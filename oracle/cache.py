@@ -1,0 +1,102 @@
+"""quantize_cache and its straight-through backward, as
+"nemo_automodel.components.models.deepseek_v41.quantization" defines them.
+
+Test infrastructure only (see ``oracle/__init__.py``).
+
+Readings taken where the page is open:
+
+* Scale rule.  The block scale is the power-of-two ceiling of amax / fmax,
+  where fmax is the largest value of the element format (6 for e2m1, 448 for
+  E4M3, "NVFP4 in the code: two scales and a nibble").  ``_power_of_two_ceiling``
+  is documented for positive normal FP32 inputs, so the ratio is formed in
+  fp32 and floored at the smallest positive normal fp32 value, 2^-126, before
+  the ceiling (an all-zero block then gets scale 2^-126 and stays zero).
+* nvfp4 stores its scale as E4M3; the powers of two E4M3 can hold are
+  2^-9 .. 2^8, so the nvfp4 scale is clamped to that range.  mxfp4 stores
+  E8M0, which holds every scale the rule can produce.  fp8's scale storage is
+  not stated; since only the round-tripped values are returned it is an fp32
+  power of two.  (No clamp binds on the seeded workloads.)
+* A final partial group is padded with zeros (page: ``quantize_cache``,
+  parameter ``values``); padding cannot change a group's amax, and is dropped
+  again from the output.
+* e2m1 elements decode through the table, so a code-8 element comes back as
+  +0.0; fp8 keeps the sign of zero.  The fake-quant value (grid value times
+  scale) is rounded nearest-even to the input dtype.
+* Any block size is accepted for every format; the page uses 32 for SWA and the
+  indexer and 16 for compressed KV.
+"""
+
+import numpy as np
+
+from .formats import E2M1_TABLE, E2M1_MAX, E4M3_MAX, e2m1_encode, e4m3_round, to_dtype_bits
+
+FORMAT_FMAX = {"fp8": E4M3_MAX, "mxfp4": E2M1_MAX, "nvfp4": E2M1_MAX}
+SMALLEST_NORMAL_F32 = 2.0 ** -126
+NVFP4_SCALE_MIN = 2.0 ** -9   # smallest power of two E4M3 holds (a subnormal)
+NVFP4_SCALE_MAX = 2.0 ** 8    # largest power of two E4M3 holds
+
+
+def power_of_two_ceiling(value):
+    """``_power_of_two_ceiling``: the smallest integer power of two that is >= value,
+    for positive normal fp32 values."""
+    v = np.asarray(value, dtype=np.float64)
+    if np.any(~(v >= SMALLEST_NORMAL_F32)) or np.any(~np.isfinite(v)):
+        raise ValueError("power_of_two_ceiling: needs positive normal finite inputs")
+    f, ex = np.frexp(v)                     # v = f * 2^ex, f in [0.5, 1)
+    # v is already a power of two exactly when f == 0.5
+    return np.where(f == 0.5, v, np.ldexp(1.0, ex))
+
+
+def cache_scale(amax, fmt):
+    """Per-block scale of ``quantize_cache`` for format ``fmt``."""
+    amax32 = np.asarray(amax, dtype=np.float32)
+    ratio = (amax32 / np.float32(FORMAT_FMAX[fmt])).astype(np.float64)   # fp32 division
+    s = power_of_two_ceiling(np.maximum(ratio, SMALLEST_NORMAL_F32))
+    if fmt == "nvfp4":
+        s = np.clip(s, NVFP4_SCALE_MIN, NVFP4_SCALE_MAX)
+    return s
+
+
+def quantize_cache_values(x, fmt, block_size):
+    """Fake-quantized values (exact, float64) of x: float64 [..., C].
+
+    Steps in the page's order: zero-pad the channel dim to whole groups of
+    ``block_size``; per group take amax and the power-of-two scale; divide;
+    round each element to the format's grid (e2m1 via the midpoint cast and the
+    table, or E4M3); multiply the scale back; drop the padding.
+    """
+    if fmt not in FORMAT_FMAX:
+        raise ValueError("quantize_cache: format must be fp8, mxfp4 or nvfp4")
+    if block_size <= 0:
+        raise ValueError("quantize_cache: block_size must be positive")
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("quantize_cache: non-finite input")
+    C = x.shape[-1]
+    lead = x.shape[:-1]
+    groups = -(-C // block_size)
+    padded = np.zeros(lead + (groups * block_size,), dtype=np.float64)
+    padded[..., :C] = x
+    blocks = padded.reshape(lead + (groups, block_size))
+    amax = np.max(np.abs(blocks), axis=-1) if C else np.zeros(lead + (0,))
+    s = cache_scale(amax, fmt)[..., None]
+    q = blocks / s                                # exact: s is a power of two
+    if fmt == "fp8":
+        grid = e4m3_round(q)
+    else:
+        grid = E2M1_TABLE[e2m1_encode(q)]
+    out = (grid * s).reshape(lead + (groups * block_size,))
+    return out[..., :C]
+
+
+def quantize_cache(x, fmt, block_size, dtype):
+    """``quantize_cache`` on exact input values x (float64 [..., C]) of a tensor
+    of ``dtype`` ('f32' | 'bf16' | 'f16'); returns raw bit patterns of a new
+    tensor of the same shape and dtype.  The input array is not modified."""
+    return to_dtype_bits(quantize_cache_values(x, fmt, block_size), dtype)
+
+
+def quantize_cache_backward(grad):
+    """``_CacheQuantization.backward``: the incoming gradient passes through
+    unchanged (straight-through); block_size and format get no gradient."""
+    return grad, None, None

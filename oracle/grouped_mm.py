@@ -1,0 +1,87 @@
+"""MXFP4GroupedMM forward and activation backward, as
+"nemo_automodel.components.quantization.mxfp4" (class ``MXFP4GroupedMM``) defines them.
+
+Test infrastructure only (see ``oracle/__init__.py``).  float64 throughout.
+
+* Weights are [E, N, K] packed along K ([E, N, K/2] int8 plus [E, N, K/32]
+  E8M0) and dequantized exactly (``dequantize_mxfp4``).
+* ``offs`` holds cumulative token counts: expert e owns rows
+  [offs[e-1], offs[e]) of the activations, with offs[-1] read as 0.
+* Forward: y[rows_e] = x[rows_e] @ W_e^T.  Backward: grad_x[rows_e] =
+  grad_out[rows_e] @ W_e, from a fresh dequantization; no weight gradient.
+* Reading: rows at or past offs[E-1] belong to no expert; they are returned as
+  zeros (the page leaves them unspecified).
+"""
+
+import numpy as np
+
+from .mxfp4 import dequantize_mxfp4_values
+
+
+def segments(offs, tokens):
+    """[(e, start, end)] for every expert; checks the offsets' preconditions
+    (non-decreasing, non-negative, last <= tokens)."""
+    offs = np.asarray(offs, dtype=np.int64)
+    out = []
+    start = 0
+    for e, end in enumerate(offs.tolist()):
+        if end < start or end > tokens:
+            raise ValueError("offs must be non-decreasing cumulative counts <= tokens")
+        out.append((e, start, end))
+        start = end
+    return out
+
+
+def _covered(offs):
+    """Number of leading rows that belong to some expert (offs[E-1], or 0)."""
+    offs = np.asarray(offs, dtype=np.int64)
+    return int(offs[-1]) if offs.size else 0
+
+
+def dequantize_expert_weights(packed, scales, expert):
+    """Exact float64 W_e [N, K] of one expert."""
+    return dequantize_mxfp4_values(packed[expert], scales[expert])
+
+
+def grouped_mm_fwd(x, packed, scales, offs, rows=None):
+    """y = x @ W_e^T per expert segment.  x: float64 [T, K].  Returns float64 [T, N].
+
+    ``rows`` (optional sorted int array) restricts the computation to those
+    output rows (others are left as NaN) so full-size workloads can be sampled.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    T, K = x.shape
+    E, N, K2 = packed.shape
+    if K2 * 2 != K:
+        raise ValueError("grouped_mm_fwd: packed must be [E, N, K/2]")
+    y = np.zeros((T, N)) if rows is None else np.full((T, N), np.nan)
+    if rows is not None:
+        y[rows[rows >= _covered(offs)]] = 0.0
+    for e, s, t in segments(offs, T):
+        sel = np.arange(s, t) if rows is None else rows[(rows >= s) & (rows < t)]
+        if len(sel) == 0:
+            continue
+        w = dequantize_expert_weights(packed, scales, e)           # [N, K]
+        y[sel] = x[sel] @ w.T
+    return y
+
+
+def grouped_mm_bwd_x(grad_out, packed, scales, offs, rows=None):
+    """grad_x = grad_out @ W_e per expert segment.  grad_out: float64 [T, N].
+    Returns float64 [T, K]; ``rows`` as in ``grouped_mm_fwd``."""
+    g = np.asarray(grad_out, dtype=np.float64)
+    T, N = g.shape
+    E, N2, K2 = packed.shape
+    if N2 != N:
+        raise ValueError("grouped_mm_bwd_x: packed must be [E, N, K/2]")
+    K = 2 * K2
+    gx = np.zeros((T, K)) if rows is None else np.full((T, K), np.nan)
+    if rows is not None:
+        gx[rows[rows >= _covered(offs)]] = 0.0
+    for e, s, t in segments(offs, T):
+        sel = np.arange(s, t) if rows is None else rows[(rows >= s) & (rows < t)]
+        if len(sel) == 0:
+            continue
+        w = dequantize_expert_weights(packed, scales, e)           # [N, K]
+        gx[sel] = g[sel] @ w
+    return gx

@@ -1,0 +1,126 @@
+"""Pins for oracle/grouped_mm.py: a pure-Python triple loop on tiny inputs, a
+row-by-row formulation that finds each row's expert from the offsets, exact
+one-hot weights, the adjoint identity <fwd(x), g> = <x, bwd(g)>, empty experts
+and uncovered rows."""
+
+import bisect
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.mxfp4 import dequantize_mxfp4_values
+
+
+def rand_weights(g, E, N, K, lo=117, hi=123):
+    packed = g.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8).view(np.int8)
+    scales = g.integers(lo, hi + 1, size=(E, N, K // 32), dtype=np.uint8)
+    return packed, scales
+
+
+def test_single_expert_matches_triple_loop():
+    g = np.random.default_rng(0)
+    T, N, K = 5, 3, 64
+    packed, scales = rand_weights(g, 1, N, K)
+    x = g.standard_normal((T, K))
+    W = dequantize_mxfp4_values(packed[0], scales[0])
+    y = oracle.grouped_mm_fwd(x, packed, scales, np.array([T], np.int32))
+    for t in range(T):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += x[t, k] * W[n, k]
+            assert abs(y[t, n] - acc) <= 1e-12 * max(1.0, abs(acc))
+    go = g.standard_normal((T, N))
+    gx = oracle.grouped_mm_bwd_x(go, packed, scales, np.array([T], np.int32))
+    for t in range(T):
+        for k in range(K):
+            acc = sum(go[t, n] * W[n, k] for n in range(N))
+            assert abs(gx[t, k] - acc) <= 1e-12 * max(1.0, abs(acc))
+
+
+def test_rowwise_formulation_with_empty_experts():
+    g = np.random.default_rng(1)
+    E, T, N, K = 4, 23, 6, 96
+    packed, scales = rand_weights(g, E, N, K)
+    offs = np.array([7, 7, 19, 21], np.int32)        # expert 1 empty; rows 21, 22 uncovered
+    x = g.standard_normal((T, K))
+    go = g.standard_normal((T, N))
+    y = oracle.grouped_mm_fwd(x, packed, scales, offs)
+    gx = oracle.grouped_mm_bwd_x(go, packed, scales, offs)
+    Ws = [dequantize_mxfp4_values(packed[e], scales[e]) for e in range(E)]
+    for t in range(T):
+        e = bisect.bisect_right(offs.tolist(), t)   # first expert whose end is past t
+        if e == E:
+            assert np.all(y[t] == 0) and np.all(gx[t] == 0)
+            continue
+        assert np.allclose(y[t], Ws[e] @ x[t], rtol=1e-12, atol=1e-12)
+        assert np.allclose(gx[t], go[t] @ Ws[e], rtol=1e-12, atol=1e-12)
+
+
+def test_one_hot_weights_are_exact():
+    """W_e[n, (n+e) mod K] = 2^(s_e - 127) (code 2 = 1.0), everything else code 0:
+    every output is one input times a power of two."""
+    E, T, N, K = 3, 12, 40, 64
+    g = np.random.default_rng(2)
+    codes = np.zeros((E, N, K), np.uint8)
+    sbyte = np.array([120, 127, 131], np.uint8)
+    for e in range(E):
+        for n in range(N):
+            codes[e, n, (n + e) % K] = 2
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8).view(np.int8)
+    scales = np.repeat(sbyte[:, None, None], N, axis=1).repeat(K // 32, axis=2)
+    offs = np.array([4, 9, 12], np.int32)
+    x = g.standard_normal((T, K))
+    y = oracle.grouped_mm_fwd(x, packed, scales, offs)
+    start = 0
+    for e in range(E):
+        for t in range(start, offs[e]):
+            for n in range(N):
+                assert y[t, n] == x[t, (n + e) % K] * 2.0 ** (int(sbyte[e]) - 127)
+        start = offs[e]
+    go = g.standard_normal((T, N))
+    gx = oracle.grouped_mm_bwd_x(go, packed, scales, offs)
+    start = 0
+    for e in range(E):
+        for t in range(start, offs[e]):
+            want = np.zeros(K)
+            for n in range(N):
+                want[(n + e) % K] += go[t, n] * 2.0 ** (int(sbyte[e]) - 127)
+            assert np.array_equal(gx[t], want)
+        start = offs[e]
+
+
+def test_adjoint_identity():
+    """Forward and activation-backward are adjoint per segment:
+    sum(fwd(x) * g) == sum(x * bwd(g)).  A transposed operand breaks it when N != K."""
+    g = np.random.default_rng(3)
+    E, T, N, K = 3, 50, 48, 160
+    packed, scales = rand_weights(g, E, N, K)
+    offs = np.array([10, 30, 50], np.int32)
+    x, go = g.standard_normal((T, K)), g.standard_normal((T, N))
+    lhs = np.sum(oracle.grouped_mm_fwd(x, packed, scales, offs) * go)
+    rhs = np.sum(x * oracle.grouped_mm_bwd_x(go, packed, scales, offs))
+    assert abs(lhs - rhs) <= 1e-9 * max(1.0, abs(lhs))
+
+
+def test_sampled_rows_match_full():
+    g = np.random.default_rng(4)
+    E, T, N, K = 3, 40, 16, 64
+    packed, scales = rand_weights(g, E, N, K)
+    offs = np.array([5, 5, 33], np.int32)
+    x = g.standard_normal((T, K))
+    full = oracle.grouped_mm_fwd(x, packed, scales, offs)
+    rows = np.array([0, 4, 5, 20, 32, 33, 39])
+    part = oracle.grouped_mm_fwd(x, packed, scales, offs, rows=rows)
+    assert np.array_equal(part[rows], full[rows])
+
+
+def test_offsets_preconditions():
+    g = np.random.default_rng(5)
+    packed, scales = rand_weights(g, 2, 4, 32)
+    x = g.standard_normal((6, 32))
+    with pytest.raises(ValueError):
+        oracle.grouped_mm_fwd(x, packed, scales, np.array([4, 3], np.int32))
+    with pytest.raises(ValueError):
+        oracle.grouped_mm_fwd(x, packed, scales, np.array([4, 7], np.int32))
