@@ -1,0 +1,142 @@
+/*
+ * mxq.h -- C ABI of libmxq: block-scaled microscaling quantization and the
+ * MXFP4 grouped GEMM, hand-written HIP for gfx950 (MI355X).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer is DEVICE memory owned by the caller.  The library
+ *    never allocates, frees or synchronizes; each call enqueues its kernels on
+ *    `stream` (a hipStream_t passed as void*; NULL = the null stream) and
+ *    returns immediately.
+ *  - Tensors are dense and row-major; leading dimensions are flattened into
+ *    `rows` by the caller.  Any alignment is accepted (misaligned or oddly
+ *    shaped tensors take a slower general kernel).
+ *  - Zero-sized problems return MXQ_OK without launching anything.
+ *  - Arguments are validated on the host before any HIP call; a failed check
+ *    returns a negative mxq_status and enqueues nothing.  A launch failure
+ *    returns MXQ_ERR_HIP.  Nothing is ever thrown across the ABI.
+ *  - Values must be finite where the operation takes an amax (NaN/Inf inputs
+ *    are outside the method's domain; the result for such a block is
+ *    unspecified but the call is memory-safe).
+ *
+ * Sources (page title, then the section on it):
+ *   [MX]  "nemo_automodel.components.quantization.mxfp4" (NeMo AutoModel API)
+ *   [QC]  "nemo_automodel.components.models.deepseek_v41.quantization"
+ *   [MO]  "NVIDIA Model Optimizer: from mtq.quantize to a 4.95-bit
+ *          DeepSeek-R1", section "NVFP4 in the code: two scales and a nibble"
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXQ_OK = 0,
+  MXQ_ERR_NULL = -1,    /* a required pointer is NULL                          */
+  MXQ_ERR_SHAPE = -2,   /* negative size, K % 32 != 0, or inconsistent sizes    */
+  MXQ_ERR_DTYPE = -3,   /* dtype code not supported by this entry point        */
+  MXQ_ERR_FORMAT = -4,  /* format code not one of mxq_format                   */
+  MXQ_ERR_BLOCK = -5,   /* block_size <= 0                                     */
+  MXQ_ERR_ALIGN = -6,   /* (reserved)                                          */
+  MXQ_ERR_ALIAS = -7,   /* output overlaps an input that must stay unmodified  */
+  MXQ_ERR_HIP = -8      /* a HIP launch reported an error                      */
+} mxq_status;
+
+typedef enum { MXQ_F32 = 0, MXQ_BF16 = 1, MXQ_F16 = 2 } mxq_dtype;
+typedef enum { MXQ_FMT_FP8 = 0, MXQ_FMT_MXFP4 = 1, MXQ_FMT_NVFP4 = 2 } mxq_format;
+
+/*
+ * quantize_mxfp4 -- [MX] quantize_mxfp4.
+ * Quantizes x [rows, k] (dtype xt: f32, bf16 or f16) along its last dim in
+ * blocks of 32 columns ([MX] MXFP4_BLOCK_SIZE).  Per block: amax = max |x|;
+ * scale exponent e = floor(log2(amax)) - 2, exact, clamped to [-127, 127],
+ * with e = -127 for an all-zero block; every element is rounded to the e2m1
+ * grid {0, .5, 1, 1.5, 2, 3, 4, 6} by the midpoints of [MX] _FP4_E2M1_MIDPOINTS,
+ * ties to the even grid value ([MO]), saturating at 6; the sign bit is set for
+ * x < 0.
+ * Outputs: packed [rows, k/2] (two codes per byte, even column in the low
+ * nibble, [MX] module docstring) and scales [rows, k/32] (E8M0 bytes e + 127).
+ * Errors: MXQ_ERR_NULL, MXQ_ERR_SHAPE (rows < 0, k < 0 or k % 32 != 0),
+ * MXQ_ERR_DTYPE, MXQ_ERR_ALIAS (outputs overlap x).
+ */
+int quantize_mxfp4(const void* x, int xt, int64_t rows, int64_t k,
+                   int8_t* packed, uint8_t* scales, void* stream);
+
+/*
+ * dequantize_mxfp4 -- [MX] dequantize_mxfp4.
+ * out[r, j] = TABLE[nibble(packed[r, j/2], j%2)] * 2^(scales[r, j/32] - 127),
+ * computed exactly and rounded nearest-even to `ot` (f32, bf16 or f16).
+ * TABLE is [MX] _FP4_E2M1_TABLE; code 8 decodes to +0.0.  Scale byte 0xFF
+ * decodes to NaN (float8_e8m0fnu); results past the output range become inf.
+ * packed [rows, k/2], scales [rows, k/32], out [rows, k].
+ * Errors: MXQ_ERR_NULL, MXQ_ERR_SHAPE, MXQ_ERR_DTYPE, MXQ_ERR_ALIAS.
+ */
+int dequantize_mxfp4(const int8_t* packed, const uint8_t* scales, int64_t rows, int64_t k,
+                     void* out, int ot, void* stream);
+
+/*
+ * quantize_cache -- [QC] quantize_cache / _CacheQuantization.forward.
+ * Fake-quantizes x [rows, channels] (dtype t) into a new tensor out of the
+ * same shape and dtype, in groups of `block_size` consecutive channels; a
+ * final partial group is treated as zero-padded.  Per group: scale s =
+ * power-of-two ceiling of max(fp32(amax / fmax), 2^-126) ([QC]
+ * _power_of_two_ceiling), fmax = 6 for mxfp4/nvfp4 and 448 for fp8 ([MO]);
+ * nvfp4 clamps s to the E4M3-representable powers 2^-9 .. 2^8.  Each element
+ * becomes grid(x / s) * s rounded to t, where grid is the e2m1 cast (as in
+ * quantize_mxfp4; code 8 gives +0.0) or nearest-even E4M3 (keeps the sign).
+ * x is not modified; out must not overlap x.
+ * Errors: MXQ_ERR_NULL, MXQ_ERR_SHAPE, MXQ_ERR_DTYPE, MXQ_ERR_FORMAT,
+ * MXQ_ERR_BLOCK, MXQ_ERR_ALIAS.
+ */
+int quantize_cache(const void* x, void* out, int t, int64_t rows, int64_t channels,
+                   int fmt, int32_t block_size, void* stream);
+
+/*
+ * quantize_cache_bwd -- [QC] _CacheQuantization.backward (straight-through).
+ * grad_in = grad_out, bit for bit, numel elements of dtype t.  When the two
+ * pointers are equal nothing is launched.  Partially overlapping buffers are
+ * rejected with MXQ_ERR_ALIAS.
+ */
+int quantize_cache_bwd(const void* grad_out, void* grad_in, int t, int64_t numel, void* stream);
+
+/*
+ * mxfp4_grouped_mm_fwd -- [MX] MXFP4GroupedMM.forward.
+ * x bf16 [tokens, k] grouped contiguously by expert; packed [experts, n, k/2]
+ * and scales [experts, n, k/32] (mxfp4 weights W_e [n, k], packed along k);
+ * offs int32 [experts] DEVICE array of cumulative token counts: expert e owns
+ * rows [offs[e-1], offs[e]) (offs[-1] = 0).  Computes y[rows_e] = x[rows_e] @
+ * W_e^T into y bf16 [tokens, n]: weights are dequantized on the fly (never
+ * written to memory), products accumulate in fp32, output rounds nearest-even.
+ * Rows at or past offs[experts-1] are written as zeros.
+ * Preconditions not checked (they would need a device sync): offs is
+ * non-decreasing and offs[experts-1] <= tokens.
+ * Errors: MXQ_ERR_NULL, MXQ_ERR_SHAPE (k % 32 != 0, negative sizes).
+ */
+int mxfp4_grouped_mm_fwd(const void* x, int64_t tokens, int64_t k,
+                         const int8_t* packed, const uint8_t* scales, int64_t experts, int64_t n,
+                         const int32_t* offs, void* y, void* stream);
+
+/*
+ * mxfp4_grouped_mm_bwd_x -- [MX] MXFP4GroupedMM.backward.
+ * grad_out bf16 [tokens, n]; weights and offs as in the forward.  Computes
+ * grad_x[rows_e] = grad_out[rows_e] @ W_e into grad_x bf16 [tokens, k], with
+ * a fresh on-the-fly dequantization; no weight gradient (frozen base).
+ * Rows past offs[experts-1] are written as zeros.  Same preconditions and
+ * errors as the forward.
+ */
+int mxfp4_grouped_mm_bwd_x(const void* grad_out, int64_t tokens, int64_t n,
+                           const int8_t* packed, const uint8_t* scales, int64_t experts, int64_t k,
+                           const int32_t* offs, void* grad_x, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* mxq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

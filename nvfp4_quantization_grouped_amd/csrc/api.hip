@@ -1,0 +1,120 @@
+// C ABI of libmxq (declared in include/mxq.h): host-side validation, then
+// one asynchronous launch on the caller's stream.  No allocation, no sync.
+#include "../../include/mxq.h"
+#include "launch.hpp"
+
+namespace {
+
+bool dtype_ok(int t) { return t == MXQ_F32 || t == MXQ_BF16 || t == MXQ_F16; }
+int64_t dtype_bytes(int t) { return t == MXQ_F32 ? 4 : 2; }
+
+// Do [a, a + na) and [b, b + nb) overlap?
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return na > 0 && nb > 0 && pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int quantize_mxfp4(const void* x, int xt, int64_t rows, int64_t k, int8_t* packed, uint8_t* scales, void* stream) {
+  if (rows < 0 || k < 0 || k % 32 != 0) return MXQ_ERR_SHAPE;
+  if (!dtype_ok(xt)) return MXQ_ERR_DTYPE;
+  if (rows == 0 || k == 0) return MXQ_OK;
+  if (!x || !packed || !scales) return MXQ_ERR_NULL;
+  const int64_t n = rows * k;
+  if (overlap(x, n * dtype_bytes(xt), packed, n / 2) || overlap(x, n * dtype_bytes(xt), scales, n / 32) ||
+      overlap(packed, n / 2, scales, n / 32))
+    return MXQ_ERR_ALIAS;
+  return from_hip(mxq::launch_quantize_mxfp4(x, xt, rows, k, packed, scales, (hipStream_t)stream));
+}
+
+int dequantize_mxfp4(const int8_t* packed, const uint8_t* scales, int64_t rows, int64_t k, void* out, int ot,
+                     void* stream) {
+  if (rows < 0 || k < 0 || k % 32 != 0) return MXQ_ERR_SHAPE;
+  if (!dtype_ok(ot)) return MXQ_ERR_DTYPE;
+  if (rows == 0 || k == 0) return MXQ_OK;
+  if (!packed || !scales || !out) return MXQ_ERR_NULL;
+  const int64_t n = rows * k;
+  if (overlap(out, n * dtype_bytes(ot), packed, n / 2) || overlap(out, n * dtype_bytes(ot), scales, n / 32))
+    return MXQ_ERR_ALIAS;
+  return from_hip(mxq::launch_dequantize_mxfp4(packed, scales, rows, k, out, ot, (hipStream_t)stream));
+}
+
+int quantize_cache(const void* x, void* out, int t, int64_t rows, int64_t channels, int fmt, int32_t block_size,
+                   void* stream) {
+  if (rows < 0 || channels < 0) return MXQ_ERR_SHAPE;
+  if (!dtype_ok(t)) return MXQ_ERR_DTYPE;
+  if (fmt != MXQ_FMT_FP8 && fmt != MXQ_FMT_MXFP4 && fmt != MXQ_FMT_NVFP4) return MXQ_ERR_FORMAT;
+  if (block_size <= 0) return MXQ_ERR_BLOCK;
+  if (rows == 0 || channels == 0) return MXQ_OK;
+  if (!x || !out) return MXQ_ERR_NULL;
+  const int64_t bytes = rows * channels * dtype_bytes(t);
+  if (overlap(x, bytes, out, bytes)) return MXQ_ERR_ALIAS;
+  return from_hip(mxq::launch_quantize_cache(x, out, t, rows, channels, fmt, block_size, (hipStream_t)stream));
+}
+
+int quantize_cache_bwd(const void* grad_out, void* grad_in, int t, int64_t numel, void* stream) {
+  if (numel < 0) return MXQ_ERR_SHAPE;
+  if (!dtype_ok(t)) return MXQ_ERR_DTYPE;
+  if (numel == 0) return MXQ_OK;
+  if (!grad_out || !grad_in) return MXQ_ERR_NULL;
+  if (grad_out == grad_in) return MXQ_OK;   // already the identity
+  const int64_t bytes = numel * dtype_bytes(t);
+  if (overlap(grad_out, bytes, grad_in, bytes)) return MXQ_ERR_ALIAS;
+  return from_hip(mxq::launch_copy(grad_out, grad_in, bytes, (hipStream_t)stream));
+}
+
+static int grouped_mm_check(const void* a, int64_t tokens, int64_t red, const int8_t* packed, const uint8_t* scales,
+                            int64_t experts, int64_t other, const int32_t* offs, void* out, int64_t k, int64_t n) {
+  if (tokens < 0 || red < 0 || other < 0 || experts < 0) return MXQ_ERR_SHAPE;
+  if (k % 32 != 0 || n % 8 != 0) return MXQ_ERR_SHAPE;
+  if (tokens > 0 && other > 0 && (!a || !out || (experts > 0 && (!packed || !scales || !offs)))) return MXQ_ERR_NULL;
+  if (((uintptr_t)a & 15) || ((uintptr_t)packed & 15)) return MXQ_ERR_ALIGN;
+  if (overlap(a, tokens * red * 2, out, tokens * other * 2)) return MXQ_ERR_ALIAS;
+  return MXQ_OK;
+}
+
+int mxfp4_grouped_mm_fwd(const void* x, int64_t tokens, int64_t k, const int8_t* packed, const uint8_t* scales,
+                         int64_t experts, int64_t n, const int32_t* offs, void* y, void* stream) {
+  const int st = grouped_mm_check(x, tokens, k, packed, scales, experts, n, offs, y, k, n);
+  if (st != MXQ_OK) return st;
+  if (tokens == 0 || n == 0) return MXQ_OK;
+  if (k == 0 || experts == 0) {   // nothing to reduce / no expert owns any row: y = 0
+    return from_hip(mxq::launch_zero(y, tokens * n * 2, (hipStream_t)stream));
+  }
+  return from_hip(mxq::launch_grouped_mm(false, x, tokens, packed, scales, experts, n, k, offs, y, (hipStream_t)stream));
+}
+
+int mxfp4_grouped_mm_bwd_x(const void* grad_out, int64_t tokens, int64_t n, const int8_t* packed,
+                           const uint8_t* scales, int64_t experts, int64_t k, const int32_t* offs, void* grad_x,
+                           void* stream) {
+  const int st = grouped_mm_check(grad_out, tokens, n, packed, scales, experts, k, offs, grad_x, k, n);
+  if (st != MXQ_OK) return st;
+  if (tokens == 0 || k == 0) return MXQ_OK;
+  if (n == 0 || experts == 0) {
+    return from_hip(mxq::launch_zero(grad_x, tokens * k * 2, (hipStream_t)stream));
+  }
+  return from_hip(
+      mxq::launch_grouped_mm(true, grad_out, tokens, packed, scales, experts, n, k, offs, grad_x, (hipStream_t)stream));
+}
+
+const char* mxq_status_string(int s) {
+  switch (s) {
+    case MXQ_OK: return "ok";
+    case MXQ_ERR_NULL: return "null pointer";
+    case MXQ_ERR_SHAPE: return "bad shape (negative size, k not a multiple of 32, or n not a multiple of 8)";
+    case MXQ_ERR_DTYPE: return "unsupported dtype";
+    case MXQ_ERR_FORMAT: return "unknown format (fp8, mxfp4 or nvfp4)";
+    case MXQ_ERR_BLOCK: return "block_size must be positive";
+    case MXQ_ERR_ALIGN: return "misaligned pointer (grouped GEMM operands need 16-byte alignment)";
+    case MXQ_ERR_ALIAS: return "output overlaps an input";
+    case MXQ_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,24 @@
+// Host-side launchers of the libmxq kernels (internal; the public ABI is
+// include/mxq.h).  Each launcher enqueues on `st` and returns the HIP error
+// of the launch.  Arguments are validated by the ABI layer before these run.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+hipError_t launch_quantize_mxfp4(const void* x, int dt, int64_t rows, int64_t k, int8_t* packed, uint8_t* scales,
+                                 hipStream_t st);
+hipError_t launch_dequantize_mxfp4(const int8_t* packed, const uint8_t* scales, int64_t rows, int64_t k, void* out,
+                                   int dt, hipStream_t st);
+hipError_t launch_quantize_cache(const void* x, void* out, int dt, int64_t rows, int64_t channels, int fmt,
+                                 int32_t block, hipStream_t st);
+hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
+hipError_t launch_zero(void* dst, int64_t bytes, hipStream_t st);
+// bwd = false: out[T, N] = a[T, K] W_e^T;  bwd = true: out[T, K] = a[T, N] W_e.
+hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8_t* packed, const uint8_t* scales,
+                             int64_t experts, int64_t wn_dim, int64_t wk_dim, const int32_t* offs, void* out,
+                             hipStream_t st);
+
+}  // namespace mxq

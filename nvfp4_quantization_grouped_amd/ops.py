@@ -1,0 +1,200 @@
+"""PyTorch-facing binding of libmxq.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C
+ABI (``include/mxq.h``).  Tensors must be CUDA (ROCm) tensors on one device;
+the call is enqueued on the current stream, outputs are allocated with
+PyTorch's caching allocator.  There is no CPU path.
+
+Names and signatures follow the pages:
+* "nemo_automodel.components.quantization.mxfp4": ``quantize_mxfp4``,
+  ``dequantize_mxfp4``, ``MXFP4GroupedMM``, ``MXFP4_BLOCK_SIZE``.
+* "nemo_automodel.components.models.deepseek_v41.quantization":
+  ``quantize_cache`` and ``_CacheQuantization``.
+"""
+
+import torch
+
+from . import _lib
+
+MXFP4_BLOCK_SIZE = 32
+
+_DT = {torch.float32: _lib.MXQ_F32, torch.bfloat16: _lib.MXQ_BF16, torch.float16: _lib.MXQ_F16}
+_FMT = {"fp8": _lib.MXQ_FMT_FP8, "mxfp4": _lib.MXQ_FMT_MXFP4, "nvfp4": _lib.MXQ_FMT_NVFP4}
+_E8M0 = getattr(torch, "float8_e8m0fnu", None)
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t):
+    return t.data_ptr() if t.numel() else None
+
+
+def _need_cuda(*ts):
+    dev = None
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("libmxq ops take GPU tensors only (there is no CPU implementation)")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+    return dev
+
+
+def _as_u8(scales):
+    if _E8M0 is not None and scales.dtype == _E8M0:
+        return scales.view(torch.uint8)
+    if scales.dtype != torch.uint8:
+        raise TypeError("scales must be float8_e8m0fnu or uint8 E8M0 bytes")
+    return scales
+
+
+def quantize_mxfp4(weight):
+    """[..., K] float tensor (K % 32 == 0) -> (int8 packed [..., K/2],
+    float8_e8m0fnu scales [..., K/32])."""
+    _need_cuda(weight)
+    if weight.dtype not in _DT:
+        raise TypeError(f"quantize_mxfp4: unsupported dtype {weight.dtype}")
+    K = weight.shape[-1]
+    if K % MXFP4_BLOCK_SIZE:
+        raise ValueError("quantize_mxfp4: K must be divisible by 32")
+    x = weight.contiguous()
+    rows = x.numel() // K if K else 0
+    packed = torch.empty(*x.shape[:-1], K // 2, dtype=torch.int8, device=x.device)
+    scales = torch.empty(*x.shape[:-1], K // 32, dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        st = _lib.lib().quantize_mxfp4(_ptr(x), _DT[x.dtype], rows, K, _ptr(packed), _ptr(scales), _stream(x.device))
+    _lib.check(st, "quantize_mxfp4")
+    return packed, (scales.view(_E8M0) if _E8M0 is not None else scales)
+
+
+def dequantize_mxfp4(packed, scales, dtype):
+    """int8 packed [..., K/2] + E8M0 scales [..., K/32] -> [..., K] in ``dtype``."""
+    _need_cuda(packed, scales)
+    if dtype not in _DT:
+        raise TypeError(f"dequantize_mxfp4: unsupported dtype {dtype}")
+    s = _as_u8(scales).contiguous()
+    p = packed.contiguous()
+    K = p.shape[-1] * 2
+    if tuple(s.shape) != tuple(p.shape[:-1]) + (K // 32,):
+        raise ValueError("dequantize_mxfp4: scales must be [..., K/32] for packed [..., K/2]")
+    rows = p.numel() * 2 // K if K else 0
+    out = torch.empty(*p.shape[:-1], K, dtype=dtype, device=p.device)
+    with torch.cuda.device(p.device):
+        st = _lib.lib().dequantize_mxfp4(_ptr(p), _ptr(s), rows, K, _ptr(out), _DT[dtype], _stream(p.device))
+    _lib.check(st, "dequantize_mxfp4")
+    return out
+
+
+def quantize_cache_forward(values, format, block_size):
+    """Fake-quantized copy of ``values`` [..., channels] (no autograd)."""
+    _need_cuda(values)
+    if values.dtype not in _DT:
+        raise TypeError(f"quantize_cache: unsupported dtype {values.dtype}")
+    if format not in _FMT:
+        raise ValueError("quantize_cache: format must be 'fp8', 'mxfp4' or 'nvfp4'")
+    x = values.contiguous()
+    C = x.shape[-1] if x.dim() else 1
+    rows = x.numel() // C if C else 0
+    out = torch.empty_like(x)
+    with torch.cuda.device(x.device):
+        st = _lib.lib().quantize_cache(_ptr(x), _ptr(out), _DT[x.dtype], rows, C, _FMT[format], int(block_size),
+                                       _stream(x.device))
+    _lib.check(st, "quantize_cache")
+    return out
+
+
+def quantize_cache_bwd(grad_out, grad_in=None):
+    """Straight-through backward through the C ABI: grad_in = grad_out
+    (a copy into ``grad_in`` or a new tensor; nothing to do if they alias)."""
+    _need_cuda(grad_out)
+    g = grad_out.contiguous()
+    out = torch.empty_like(g) if grad_in is None else grad_in
+    _need_cuda(out)
+    if out.dtype != g.dtype or out.numel() != g.numel() or not out.is_contiguous():
+        raise ValueError("quantize_cache_bwd: grad_in must be a contiguous tensor like grad_out")
+    with torch.cuda.device(g.device):
+        st = _lib.lib().quantize_cache_bwd(_ptr(g), _ptr(out), _DT[g.dtype], g.numel(), _stream(g.device))
+    _lib.check(st, "quantize_cache_bwd")
+    return out
+
+
+class CacheQuantization(torch.autograd.Function):
+    """``_CacheQuantization``: quantize/dequantize in forward, pass the
+    gradient through unchanged in backward (no gradient for block_size and
+    format)."""
+
+    @staticmethod
+    def forward(ctx, values, block_size, format):
+        return quantize_cache_forward(values, format, block_size)
+
+    @staticmethod
+    def backward(ctx, gradient):
+        return gradient, None, None
+
+
+def quantize_cache(values, format, block_size):
+    """``quantize_cache(values, format, block_size)``: the cache
+    quantize/dequantize round trip with a straight-through gradient."""
+    return CacheQuantization.apply(values, block_size, format)
+
+
+def _gemm_args(a, packed, scales, offs):
+    _need_cuda(a, packed, scales, offs)
+    if a.dtype != torch.bfloat16:
+        raise TypeError("MXFP4GroupedMM: activations must be bfloat16")
+    if offs.dtype != torch.int32:
+        raise TypeError("MXFP4GroupedMM: offs must be int32")
+    s = _as_u8(scales)
+    if packed.dim() != 3 or s.dim() != 3 or offs.dim() != 1:
+        raise ValueError("MXFP4GroupedMM: packed [E, N, K/2], scales [E, N, K/32], offs [E]")
+    E, N, K2 = packed.shape
+    if tuple(s.shape) != (E, N, K2 * 2 // 32) or offs.shape[0] != E:
+        raise ValueError("MXFP4GroupedMM: inconsistent packed / scales / offs shapes")
+    return a.contiguous(), packed.contiguous(), s.contiguous(), offs.contiguous(), E, N, K2 * 2
+
+
+def mxfp4_grouped_mm_fwd(x, packed, scales, offs):
+    """y [T, N] = x[rows_e] @ W_e^T per expert segment (bf16 in/out)."""
+    x, p, s, o, E, N, K = _gemm_args(x, packed, scales, offs)
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError("mxfp4_grouped_mm_fwd: x must be [tokens, K]")
+    T = x.shape[0]
+    y = torch.empty(T, N, dtype=torch.bfloat16, device=x.device)
+    with torch.cuda.device(x.device):
+        st = _lib.lib().mxfp4_grouped_mm_fwd(_ptr(x), T, K, _ptr(p), _ptr(s), E, N, _ptr(o), _ptr(y),
+                                             _stream(x.device))
+    _lib.check(st, "mxfp4_grouped_mm_fwd")
+    return y
+
+
+def mxfp4_grouped_mm_bwd_x(grad_out, packed, scales, offs):
+    """grad_x [T, K] = grad_out[rows_e] @ W_e per expert segment (bf16)."""
+    g, p, s, o, E, N, K = _gemm_args(grad_out, packed, scales, offs)
+    if g.dim() != 2 or g.shape[1] != N:
+        raise ValueError("mxfp4_grouped_mm_bwd_x: grad_out must be [tokens, N]")
+    T = g.shape[0]
+    gx = torch.empty(T, K, dtype=torch.bfloat16, device=g.device)
+    with torch.cuda.device(g.device):
+        st = _lib.lib().mxfp4_grouped_mm_bwd_x(_ptr(g), T, N, _ptr(p), _ptr(s), E, K, _ptr(o), _ptr(gx),
+                                               _stream(g.device))
+    _lib.check(st, "mxfp4_grouped_mm_bwd_x")
+    return gx
+
+
+class MXFP4GroupedMM(torch.autograd.Function):
+    """Grouped GEMM over mxfp4-packed frozen expert weights.  Saves only the
+    packed weights, scales and offsets; the backward dequantizes again inside
+    its kernel and returns (grad_x, None, None, None)."""
+
+    @staticmethod
+    def forward(ctx, x, packed, scales, offs):
+        ctx.save_for_backward(packed, scales, offs)
+        return mxfp4_grouped_mm_fwd(x, packed, scales, offs)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        packed, scales, offs = ctx.saved_tensors
+        return mxfp4_grouped_mm_bwd_x(grad_out.to(torch.bfloat16), packed, scales, offs), None, None, None

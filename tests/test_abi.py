@@ -1,0 +1,103 @@
+"""The C-ABI library loads, exports every entry point include/mxq.h declares,
+and rejects bad arguments on the host before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_quantization_grouped_amd as mxq
+from nvfp4_quantization_grouped_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmxq.so is not built (python -m nvfp4_quantization_grouped_amd.build)")
+    return mxq.lib()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+        assert isinstance(getattr(L, name), ctypes._CFuncPtr)
+
+
+def test_status_strings(L):
+    for s in range(0, -9, -1):
+        msg = L.mxq_status_string(s)
+        assert msg and msg != b"unknown status"
+    assert L.mxq_status_string(12345) == b"unknown status"
+
+
+# Host-side validation: every call below must fail before touching the GPU.
+FAKE = 0x10000            # a non-null, 16-byte aligned address that is never dereferenced
+
+
+def test_quantize_mxfp4_validation(L):
+    assert L.quantize_mxfp4(FAKE, 1, 4, 48, FAKE * 2, FAKE * 3, None) == -2      # k % 32
+    assert L.quantize_mxfp4(FAKE, 1, -1, 32, FAKE * 2, FAKE * 3, None) == -2     # rows < 0
+    assert L.quantize_mxfp4(FAKE, 7, 4, 32, FAKE * 2, FAKE * 3, None) == -3      # dtype
+    assert L.quantize_mxfp4(None, 1, 4, 32, FAKE * 2, FAKE * 3, None) == -1      # null
+    assert L.quantize_mxfp4(FAKE, 1, 4, 32, FAKE + 8, FAKE * 3, None) == -7      # packed inside x
+    assert L.quantize_mxfp4(FAKE, 1, 0, 32, None, None, None) == 0               # empty: no launch
+
+
+def test_dequantize_validation(L):
+    assert L.dequantize_mxfp4(FAKE, FAKE * 2, 4, 40, FAKE * 3, 1, None) == -2
+    assert L.dequantize_mxfp4(FAKE, FAKE * 2, 4, 32, FAKE * 3, 5, None) == -3
+    assert L.dequantize_mxfp4(FAKE, None, 4, 32, FAKE * 3, 1, None) == -1
+    assert L.dequantize_mxfp4(FAKE, FAKE * 2, 4, 32, FAKE, 1, None) == -7
+    assert L.dequantize_mxfp4(None, None, 4, 0, None, 1, None) == 0
+
+
+def test_quantize_cache_validation(L):
+    assert L.quantize_cache(FAKE, FAKE * 4, 1, 2, 64, 3, 32, None) == -4         # format
+    assert L.quantize_cache(FAKE, FAKE * 4, 1, 2, 64, 1, 0, None) == -5          # block
+    assert L.quantize_cache(FAKE, FAKE * 4, 9, 2, 64, 1, 32, None) == -3         # dtype
+    assert L.quantize_cache(FAKE, FAKE + 64, 1, 2, 64, 1, 32, None) == -7        # out overlaps x
+    assert L.quantize_cache(FAKE, None, 1, 2, 64, 1, 32, None) == -1
+    assert L.quantize_cache(FAKE, FAKE * 4, 1, -2, 64, 1, 32, None) == -2
+    assert L.quantize_cache(None, None, 1, 0, 64, 2, 16, None) == 0
+
+
+def test_quantize_cache_bwd_validation(L):
+    assert L.quantize_cache_bwd(FAKE, FAKE, 1, 100, None) == 0                   # aliased: identity
+    assert L.quantize_cache_bwd(FAKE, FAKE + 2, 1, 100, None) == -7              # partial overlap
+    assert L.quantize_cache_bwd(None, FAKE, 1, 100, None) == -1
+    assert L.quantize_cache_bwd(FAKE, FAKE * 8, 4, 100, None) == -3
+
+
+def test_grouped_mm_validation(L):
+    f = L.mxfp4_grouped_mm_fwd
+    assert f(FAKE, 16, 48, FAKE * 2, FAKE * 3, 2, 64, FAKE * 4, FAKE * 5, None) == -2    # k % 32
+    assert f(FAKE, 16, 64, FAKE * 2, FAKE * 3, 2, 60, FAKE * 4, FAKE * 5, None) == -2    # n % 8
+    assert f(FAKE, 16, 64, None, FAKE * 3, 2, 64, FAKE * 4, FAKE * 5, None) == -1
+    assert f(FAKE + 2, 16, 64, FAKE * 2, FAKE * 3, 2, 64, FAKE * 4, FAKE * 5, None) == -6  # alignment
+    assert f(FAKE, 16, 64, FAKE * 2, FAKE * 3, 2, 64, FAKE * 4, FAKE + 64, None) == -7   # y overlaps x
+    assert f(FAKE, 0, 64, FAKE * 2, FAKE * 3, 2, 64, FAKE * 4, FAKE * 5, None) == 0      # no tokens
+    b = L.mxfp4_grouped_mm_bwd_x
+    assert b(FAKE, 16, 64, FAKE * 2, FAKE * 3, 2, 40, FAKE * 4, FAKE * 5, None) == -2    # k % 32
+    assert b(FAKE, 16, 64, FAKE * 2, FAKE * 3, -1, 64, FAKE * 4, FAKE * 5, None) == -2
+
+
+def test_ops_reject_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        mxq.quantize_mxfp4(torch.zeros(2, 32))
+    with pytest.raises(ValueError):
+        mxq.quantize_cache(torch.zeros(2, 32, dtype=torch.bfloat16), "fp8", 32)

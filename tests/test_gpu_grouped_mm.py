@@ -1,0 +1,162 @@
+"""GPU parity of the MXFP4 grouped GEMM (forward and grad_x) against the
+float64 oracle: bit-exact on one-hot weights, relative Frobenius error
+<= 5e-3 per expert segment and globally on random data, ragged segments,
+empty experts, rows no expert owns, tile tails, and the full-size workloads."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import nvfp4_quantization_grouped_amd as mxq
+from tests.gpu_util import dev, from_gpu_bits, rel_frobenius, to_gpu_bits
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-3   # relative Frobenius error against the fp64 oracle
+
+
+def gpu_weights(packed, scales):
+    return torch.from_numpy(packed).to(dev()), torch.from_numpy(scales).to(dev())
+
+
+def bf16_values(t):
+    return oracle.from_dtype_bits(from_gpu_bits(t), "bf16")
+
+
+def check_segments(got, want, offs, rows=None, what=""):
+    """Global and per-expert relative Frobenius error (only over `rows` if given)."""
+    T = got.shape[0]
+    sel = np.arange(T) if rows is None else rows
+    errs = {"global": rel_frobenius(got[sel], want[sel])}
+    start = 0
+    for e, end in enumerate(np.asarray(offs).tolist()):
+        r = sel[(sel >= start) & (sel < end)]
+        if len(r):
+            errs[e] = rel_frobenius(got[r], want[r])
+        start = end
+    worst = max(errs.values())
+    assert worst <= TOL, f"{what}: rel Frobenius {worst:.3e} > {TOL} ({errs})"
+    # rows no expert owns are exactly zero
+    tail = sel[sel >= (offs[-1] if len(offs) else 0)]
+    assert np.all(got[tail] == 0), f"{what}: uncovered rows are not zero"
+    return errs
+
+
+def random_case(seed, E, T, N, K, offs):
+    d = synth.streams(seed, 3)
+    packed, scales = synth.packed_weights(d[0], d[1], E, N, K)
+    x = synth.normal_bf16(d[2], (T, K))
+    return packed, scales, x
+
+
+def test_one_hot_weights_bit_exact():
+    """W_e[n, (n+e) mod K] = 2^(s_e-127): every output is one input times a
+    power of two, so forward and backward must match the oracle bit for bit."""
+    E, T, N, K = 3, 300, 384, 512
+    codes = np.zeros((E, N, K), np.uint8)
+    for e in range(E):
+        codes[e, np.arange(N), (np.arange(N) + e) % K] = 2
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8).view(np.int8)
+    sbyte = np.array([120, 127, 131], np.uint8)
+    scales = np.repeat(np.repeat(sbyte[:, None, None], N, axis=1), K // 32, axis=2)
+    offs = np.array([70, 70, 290], np.int32)           # expert 1 empty, 10 uncovered rows
+    g = np.random.default_rng(0)
+    xb = synth.f32_to_bf16_bits(g.standard_normal((T, K)).astype(np.float32))
+    pt, st = gpu_weights(packed, scales)
+    ot = torch.from_numpy(offs).to(dev())
+    y = mxq.mxfp4_grouped_mm_fwd(to_gpu_bits(xb, "bf16"), pt, st, ot)
+    want = oracle.grouped_mm_fwd(oracle.from_dtype_bits(xb, "bf16"), packed, scales, offs)
+    assert np.array_equal(from_gpu_bits(y), oracle.to_dtype_bits(want, "bf16"))
+    gb = synth.f32_to_bf16_bits(g.standard_normal((T, N)).astype(np.float32))
+    gx = mxq.mxfp4_grouped_mm_bwd_x(to_gpu_bits(gb, "bf16"), pt, st, ot)
+    want_b = oracle.grouped_mm_bwd_x(oracle.from_dtype_bits(gb, "bf16"), packed, scales, offs)
+    # each grad_x entry is a sum of at most ceil(N/K) products of distinct columns: exact here (N < K)
+    assert np.array_equal(from_gpu_bits(gx), oracle.to_dtype_bits(want_b, "bf16"))
+
+
+@pytest.mark.parametrize("E,T,N,K,counts", [
+    (1, 64, 256, 256, [64]),                          # single expert = dense GEMM
+    (4, 777, 264, 96, [100, 0, 377, 250]),            # N, K tails; empty expert; 50 uncovered rows
+    (8, 1500, 512, 1024, [300, 1, 255, 257, 0, 0, 400, 287]),
+    (3, 600, 1024, 2048, [0, 600, 0]),
+    (5, 2048, 2048, 512, [512, 512, 512, 256, 256]),
+])
+def test_random_segments(E, T, N, K, counts):
+    offs = np.cumsum(counts).astype(np.int32)
+    packed, scales, xb = random_case(E * 1000 + T, E, T, N, K, offs)
+    pt, st = gpu_weights(packed, scales)
+    ot = torch.from_numpy(offs).to(dev())
+    x = oracle.from_dtype_bits(xb, "bf16")
+    y = mxq.mxfp4_grouped_mm_fwd(to_gpu_bits(xb, "bf16"), pt, st, ot)
+    want = oracle.grouped_mm_fwd(x, packed, scales, offs)
+    check_segments(bf16_values(y), want, offs, what="fwd")
+    gb = synth.normal_bf16(np.random.default_rng(T), (T, N), 0.1)
+    gx = mxq.mxfp4_grouped_mm_bwd_x(to_gpu_bits(gb, "bf16"), pt, st, ot)
+    want_b = oracle.grouped_mm_bwd_x(oracle.from_dtype_bits(gb, "bf16"), packed, scales, offs)
+    check_segments(bf16_values(gx), want_b, offs, what="bwd_x")
+
+
+def test_autograd_function():
+    E, T, N, K = 4, 400, 256, 512
+    offs = np.array([100, 200, 300, 400], np.int32)
+    packed, scales, xb = random_case(7, E, T, N, K, offs)
+    pt, st = gpu_weights(packed, scales)
+    ot = torch.from_numpy(offs).to(dev())
+    xt = to_gpu_bits(xb, "bf16").requires_grad_(True)
+    y = mxq.MXFP4GroupedMM.apply(xt, pt, st, ot)
+    gb = synth.normal_bf16(np.random.default_rng(8), (T, N), 0.1)
+    y.backward(to_gpu_bits(gb, "bf16"))
+    want = oracle.grouped_mm_bwd_x(oracle.from_dtype_bits(gb, "bf16"), packed, scales, offs)
+    check_segments(bf16_values(xt.grad), want, offs, what="autograd grad_x")
+    direct = mxq.mxfp4_grouped_mm_bwd_x(to_gpu_bits(gb, "bf16"), pt, st, ot)
+    assert torch.equal(direct, xt.grad)
+
+
+def test_grouped_mm_e8_workload():
+    """E=8, x bf16 [4096, 4096], weights [8, 2048, 4096] packed, multinomial counts."""
+    d = synth.grouped_mm_e8(seed=0)
+    pt, st = gpu_weights(d["packed"], d["scales"])
+    ot = torch.from_numpy(d["offs"]).to(dev())
+    y = mxq.mxfp4_grouped_mm_fwd(to_gpu_bits(d["x"], "bf16"), pt, st, ot)
+    want = oracle.grouped_mm_fwd(oracle.from_dtype_bits(d["x"], "bf16"), d["packed"], d["scales"], d["offs"])
+    errs = check_segments(bf16_values(y), want, d["offs"], what="E=8 fwd")
+    print("E=8 fwd rel Frobenius", {k: f"{v:.2e}" for k, v in errs.items()})
+
+
+@pytest.mark.timeout(900)
+def test_moe_layer_workload_sampled_rows():
+    """32 local experts, hidden 7168, intermediate 2048, 131072 routed rows
+    (Zipf-skewed, 4 idle experts): gate/up and down, forward and grad_x,
+    checked on 8 sampled rows of every non-empty expert."""
+    d = synth.moe_layer(seed=0)
+    offs = d["offs"]
+    ot = torch.from_numpy(offs).to(dev())
+    assert (d["counts"] == 0).sum() >= 4
+    g = np.random.default_rng(5)
+    rows, start = [], 0
+    for end in offs.tolist():
+        if end > start:
+            rows.append(np.sort(g.choice(np.arange(start, end), size=min(8, end - start), replace=False)))
+        start = end
+    rows = np.concatenate(rows)
+    ri = torch.from_numpy(rows).to(dev())
+
+    x_routed = to_gpu_bits(d["tokens_x"], "bf16")[torch.from_numpy(d["row_token"]).to(dev())]
+    layers = [
+        ("gate/up", d["gu_packed"], d["gu_scales"], x_routed, d["tokens_x"][d["row_token"][rows]], d["gu_grad"]),
+        ("down", d["dn_packed"], d["dn_scales"], to_gpu_bits(d["h"], "bf16"), d["h"][rows], d["dn_grad"]),
+    ]
+    for name, pk, sc, a_gpu, a_rows_bits, grad_bits in layers:
+        pt, st = gpu_weights(pk, sc)
+        y = mxq.mxfp4_grouped_mm_fwd(a_gpu, pt, st, ot)
+        gx = mxq.mxfp4_grouped_mm_bwd_x(to_gpu_bits(grad_bits, "bf16"), pt, st, ot)
+        want_y, want_gx = oracle.grouped_mm_rows(
+            rows, pk, sc, offs, x_rows=oracle.from_dtype_bits(a_rows_bits, "bf16"),
+            g_rows=oracle.from_dtype_bits(grad_bits[rows], "bf16"))
+        for what, got, want in [("fwd", bf16_values(y[ri]), want_y), ("bwd_x", bf16_values(gx[ri]), want_gx)]:
+            err = rel_frobenius(got, want)
+            print(f"{name} {what}: sampled rel Frobenius {err:.2e}")
+            assert err <= TOL, f"{name} {what}: {err:.3e}"
+        del y, gx

@@ -116,6 +116,18 @@ def test_sampled_rows_match_full():
     assert np.array_equal(part[rows], full[rows])
 
 
+def test_row_restricted_form_matches_full():
+    g = np.random.default_rng(6)
+    E, T, N, K = 4, 60, 24, 96
+    packed, scales = rand_weights(g, E, N, K)
+    offs = np.array([10, 10, 41, 55], np.int32)
+    x, go = g.standard_normal((T, K)), g.standard_normal((T, N))
+    rows = np.array([0, 9, 10, 40, 41, 54, 55, 59])
+    y, gx = oracle.grouped_mm_rows(rows, packed, scales, offs, x_rows=x[rows], g_rows=go[rows])
+    assert np.array_equal(y, oracle.grouped_mm_fwd(x, packed, scales, offs)[rows])
+    assert np.array_equal(gx, oracle.grouped_mm_bwd_x(go, packed, scales, offs)[rows])
+
+
 def test_offsets_preconditions():
     g = np.random.default_rng(5)
     packed, scales = rand_weights(g, 2, 4, 32)
