@@ -42,7 +42,7 @@ from .formats import (
 )
 from .mxfp4 import quantize_mxfp4, dequantize_mxfp4, floor_scale_exponent
 from .cache import power_of_two_ceiling, cache_scale, quantize_cache, quantize_cache_backward
-from .grouped_mm import dequantize_expert_weights, grouped_mm_fwd, grouped_mm_bwd_x, segments
+from .grouped_mm import dequantize_expert_weights, grouped_mm_fwd, grouped_mm_bwd_x, grouped_mm_rows, segments
 
 __all__ = [
     "E2M1_TABLE", "E2M1_MIDPOINTS", "MXFP4_BLOCK_SIZE", "E4M3_MAX",
@@ -50,5 +50,5 @@ __all__ = [
     "to_dtype_bits", "from_dtype_bits",
     "quantize_mxfp4", "dequantize_mxfp4", "floor_scale_exponent",
     "power_of_two_ceiling", "cache_scale", "quantize_cache", "quantize_cache_backward",
-    "dequantize_expert_weights", "grouped_mm_fwd", "grouped_mm_bwd_x", "segments",
+    "dequantize_expert_weights", "grouped_mm_fwd", "grouped_mm_bwd_x", "grouped_mm_rows", "segments",
 ]

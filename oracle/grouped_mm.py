@@ -85,3 +85,31 @@ def grouped_mm_bwd_x(grad_out, packed, scales, offs, rows=None):
         w = dequantize_expert_weights(packed, scales, e)           # [N, K]
         gx[sel] = g[sel] @ w
     return gx
+
+
+def grouped_mm_rows(rows, packed, scales, offs, x_rows=None, g_rows=None):
+    """Forward and/or activation-backward restricted to the given token rows,
+    for sampling full-size workloads: ``rows`` (sorted ints), ``x_rows`` =
+    x[rows] ([R, K]) and/or ``g_rows`` = grad_out[rows] ([R, N]).  Each expert's
+    weight is dequantized once for both products.  Returns (y[rows], grad_x[rows])
+    (None for a product not asked for); rows no expert owns give zeros."""
+    rows = np.asarray(rows, dtype=np.int64)
+    E, N, K2 = packed.shape
+    K = 2 * K2
+    y = None if x_rows is None else np.zeros((len(rows), N))
+    gx = None if g_rows is None else np.zeros((len(rows), K))
+    for e, s, t in _segments_unbounded(offs):
+        sel = np.flatnonzero((rows >= s) & (rows < t))
+        if len(sel) == 0:
+            continue
+        w = dequantize_expert_weights(packed, scales, e)
+        if y is not None:
+            y[sel] = np.asarray(x_rows, dtype=np.float64)[sel] @ w.T
+        if gx is not None:
+            gx[sel] = np.asarray(g_rows, dtype=np.float64)[sel] @ w
+    return y, gx
+
+
+def _segments_unbounded(offs):
+    offs = np.asarray(offs, dtype=np.int64)
+    return segments(offs, int(offs[-1]) if offs.size else 0)
