@@ -1,0 +1,336 @@
+"""Throughput of the block-scaled quantization / MXFP4 grouped-GEMM hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+One step runs every part of the path once, each on its own seeded synthetic
+workload, all inputs already resident in HBM:
+
+* grouped GEMM, one GPU's share of a routed-expert layer: 32 experts, hidden
+  7168, intermediate 2048, 131072 routed rows (16384 tokens x top-8,
+  Zipf(1.1)-skewed, 4 idle experts): gate/up and down forward, then down and
+  gate/up grad_x (re-dequantizing the weights);
+* grouped GEMM forward, 8 experts, x [4096, 4096], W [8, 2048, 4096];
+* quantize_cache on a bf16 KV cache [4, 8192, 512]: fp8/128, mxfp4/32,
+  nvfp4/16, and the straight-through backward copy;
+* bulk bf16 [65536, 7168]: quantize_mxfp4, dequantize_mxfp4, quantize_cache
+  nvfp4/16, fp8/128 and mxfp4/32; dequantization of a 2^30-parameter
+  mxfp4 weight [64, 4096, 4096] to bf16;
+* mxfp4 round trip of an fp32 [256, 1024] tensor (latency-bound).
+
+Legs whose working set fits in the 256 MB Infinity Cache rotate over enough
+buffer copies to exceed it.  Each leg is bracketed by HIP events recorded on
+the stream its kernels run on; `value` is the grouped-GEMM throughput of the
+routed-expert layer (algorithmic flops 2 * rows * N * K summed over its four
+GEMMs, divided by their event time); `hbm` aggregates the codec legs
+(algorithmic bytes over event time).  Prints one JSON line.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+METRIC = "quant/dequant GB/s (% HBM peak); MXFP4 grouped-GEMM TFLOP/s (% MFMA peak)"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--legs", default="all", help="comma-separated leg-name prefixes to run (profiling)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Leg:
+    def __init__(self, name, kernel, kind, work, fn, reps=1):
+        self.name, self.kernel, self.kind, self.work, self.fn, self.reps = name, kernel, kind, work, fn, reps
+        self.ms = 0.0   # summed event time over the timed steps
+
+    def run(self, step):
+        for r in range(self.reps):
+            self.fn(step * self.reps + r)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the workloads are one GPU's share; see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import synth
+    import nvfp4_quantization_grouped_amd as mxq
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    L = mxq.lib()
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    want = None if args.legs == "all" else [p.strip() for p in args.legs.split(",")]
+
+    def wanted(name):
+        return want is None or any(name.startswith(p) for p in want)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def check(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {L.mxq_status_string(st).decode()}")
+
+    legs = []
+    t_gen = time.perf_counter()
+
+    # ---------------- routed-expert layer (gate/up + down, fwd + grad_x)
+    moe = None
+    if wanted("moe"):
+        moe = synth.moe_layer(seed=0)
+        T = int(moe["offs"][-1])
+        E, H, I2, I = 32, 7168, 4096, 2048
+        offs = torch.from_numpy(moe["offs"]).to(dev)
+        gu_p, gu_s = torch.from_numpy(moe["gu_packed"]).to(dev), torch.from_numpy(moe["gu_scales"]).to(dev)
+        dn_p, dn_s = torch.from_numpy(moe["dn_packed"]).to(dev), torch.from_numpy(moe["dn_scales"]).to(dev)
+        x_routed = bf16(moe["tokens_x"])[torch.from_numpy(moe["row_token"]).to(dev)].contiguous()
+        h = bf16(moe["h"])
+        gu_g, dn_g = bf16(moe["gu_grad"]), bf16(moe["dn_grad"])
+        gu_y = torch.empty(T, I2, dtype=torch.bfloat16, device=dev)
+        dn_y = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+        dn_gx = torch.empty(T, I, dtype=torch.bfloat16, device=dev)
+        gu_gx = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+        moe_rows = int(moe["counts"].sum())
+
+        def fwd(a, p, s, n, k, y):
+            return lambda i: check(L.mxfp4_grouped_mm_fwd(a.data_ptr(), T, k, p.data_ptr(), s.data_ptr(), E, n,
+                                                          offs.data_ptr(), y.data_ptr(), sp), "fwd")
+
+        def bwd(g, p, s, n, k, gx):
+            return lambda i: check(L.mxfp4_grouped_mm_bwd_x(g.data_ptr(), T, n, p.data_ptr(), s.data_ptr(), E, k,
+                                                            offs.data_ptr(), gx.data_ptr(), sp), "bwd_x")
+
+        legs += [
+            Leg("moe.gate_up.fwd", "k_grouped_mm<256,256,fwd>", "flop", 2.0 * moe_rows * I2 * H, fwd(x_routed, gu_p, gu_s, I2, H, gu_y)),
+            Leg("moe.down.fwd", "k_grouped_mm<256,256,fwd>", "flop", 2.0 * moe_rows * H * I, fwd(h, dn_p, dn_s, H, I, dn_y)),
+            Leg("moe.down.bwd_x", "k_grouped_mm<256,256,bwd>", "flop", 2.0 * moe_rows * H * I, bwd(dn_g, dn_p, dn_s, H, I, dn_gx)),
+            Leg("moe.gate_up.bwd_x", "k_grouped_mm<256,256,bwd>", "flop", 2.0 * moe_rows * I2 * H, bwd(gu_g, gu_p, gu_s, I2, H, gu_gx)),
+        ]
+
+    # ---------------- 8-expert grouped GEMM forward (4 rotating buffer sets > 256 MB)
+    if wanted("e8"):
+        e8 = synth.grouped_mm_e8(seed=0)
+        R8 = 4
+        e8_x = [bf16(e8["x"]) for _ in range(R8)]
+        e8_p = [torch.from_numpy(e8["packed"]).to(dev) for _ in range(R8)]
+        e8_s = [torch.from_numpy(e8["scales"]).to(dev) for _ in range(R8)]
+        e8_o = torch.from_numpy(e8["offs"]).to(dev)
+        e8_y = [torch.empty(4096, 2048, dtype=torch.bfloat16, device=dev) for _ in range(R8)]
+
+        def e8_fn(i):
+            j = i % R8
+            check(L.mxfp4_grouped_mm_fwd(e8_x[j].data_ptr(), 4096, 4096, e8_p[j].data_ptr(), e8_s[j].data_ptr(), 8,
+                                         2048, e8_o.data_ptr(), e8_y[j].data_ptr(), sp), "e8 fwd")
+        legs.append(Leg("e8.fwd", "k_grouped_mm<256,128,fwd>", "flop", 2.0 * 4096 * 2048 * 4096, e8_fn, reps=R8))
+
+    # ---------------- KV cache quantize_cache x3 + STE (8 rotating sets: 8 x 64 MiB per leg)
+    if wanted("kv"):
+        kv = synth.kv_cache(seed=0)
+        R = 8
+        kv_x = [bf16(kv["x"]) for _ in range(R)]
+        kv_o = [torch.empty_like(kv_x[0]) for _ in range(R)]
+        kv_g = [bf16(kv["grad"]) for _ in range(R)]
+        kv_gi = [torch.empty_like(kv_g[0]) for _ in range(R)]
+        n_kv = kv_x[0].numel()
+        rows_kv, C_kv = n_kv // 512, 512
+        for fmt, code, block in [("fp8", 0, 128), ("mxfp4", 1, 32), ("nvfp4", 2, 16)]:
+            def f(i, code=code, block=block):
+                j = i % R
+                check(L.quantize_cache(kv_x[j].data_ptr(), kv_o[j].data_ptr(), 1, rows_kv, C_kv, code, block, sp), "kv")
+            legs.append(Leg(f"kv.quantize_cache.{fmt}", f"k_quantize_cache<bf16,{fmt},{block // 8}>", "byte",
+                            4.0 * n_kv, f, reps=R))
+
+        def ste(i):
+            j = i % R
+            check(L.quantize_cache_bwd(kv_g[j].data_ptr(), kv_gi[j].data_ptr(), 1, n_kv, sp), "ste")
+        legs.append(Leg("kv.ste_bwd", "k_copy16", "byte", 4.0 * n_kv, ste, reps=R))
+
+    # ---------------- bulk bf16 [65536, 7168] + 2^30-parameter weight dequant
+    if wanted("bulk"):
+        bulk = synth.bulk_stream(seed=0)
+        bx = bf16(bulk["x"])
+        nb = bx.numel()
+        br, bc = bx.shape
+        bpk = torch.empty(br, bc // 2, dtype=torch.int8, device=dev)
+        bsc = torch.empty(br, bc // 32, dtype=torch.uint8, device=dev)
+        bdq = torch.empty_like(bx)
+        bco = torch.empty_like(bx)
+        wp, ws = torch.from_numpy(bulk["w_packed"]).to(dev), torch.from_numpy(bulk["w_scales"]).to(dev)
+        wout = torch.empty(64, 4096, 4096, dtype=torch.bfloat16, device=dev)
+        legs.append(Leg("bulk.quantize_mxfp4", "k_quantize_mxfp4<bf16>", "byte", nb * (2 + 0.5 + 1 / 32),
+                        lambda i: check(L.quantize_mxfp4(bx.data_ptr(), 1, br, bc, bpk.data_ptr(), bsc.data_ptr(), sp), "q")))
+        legs.append(Leg("bulk.dequantize_mxfp4", "k_dequantize_mxfp4<bf16>", "byte", nb * (0.5 + 1 / 32 + 2),
+                        lambda i: check(L.dequantize_mxfp4(bpk.data_ptr(), bsc.data_ptr(), br, bc, bdq.data_ptr(), 1, sp), "dq")))
+        for fmt, code, block in [("nvfp4", 2, 16), ("fp8", 0, 128), ("mxfp4", 1, 32)]:
+            legs.append(Leg(f"bulk.quantize_cache.{fmt}", f"k_quantize_cache<bf16,{fmt},{block // 8}>", "byte", 4.0 * nb,
+                            lambda i, code=code, block=block: check(
+                                L.quantize_cache(bx.data_ptr(), bco.data_ptr(), 1, br, bc, code, block, sp), "qc")))
+        nw = 64 * 4096 * 4096
+        legs.append(Leg("bulk.weight_dequant", "k_dequantize_mxfp4<bf16>", "byte", nw * (0.5 + 1 / 32 + 2),
+                        lambda i: check(L.dequantize_mxfp4(wp.data_ptr(), ws.data_ptr(), 64 * 4096, 4096,
+                                                           wout.data_ptr(), 1, sp), "wdq")))
+
+    # ---------------- fp32 [256, 1024] round trip (latency-bound; 64 rotating sets)
+    if wanted("roundtrip"):
+        rt = synth.roundtrip_f32(seed=0)
+        RR = 64
+        rx = [torch.from_numpy(rt["x"]).to(dev) for _ in range(RR)]
+        rp = [torch.empty(256, 512, dtype=torch.int8, device=dev) for _ in range(RR)]
+        rs = [torch.empty(256, 32, dtype=torch.uint8, device=dev) for _ in range(RR)]
+        ro = [torch.empty(256, 1024, dtype=torch.float32, device=dev) for _ in range(RR)]
+
+        def rt_fn(i):
+            j = i % RR
+            check(L.quantize_mxfp4(rx[j].data_ptr(), 0, 256, 1024, rp[j].data_ptr(), rs[j].data_ptr(), sp), "rt q")
+            check(L.dequantize_mxfp4(rp[j].data_ptr(), rs[j].data_ptr(), 256, 1024, ro[j].data_ptr(), 0, sp), "rt dq")
+        legs.append(Leg("roundtrip.f32", "k_quantize_mxfp4<f32>+k_dequantize_mxfp4<f32>", "byte",
+                        2 * 262144 * (4 + 0.5 + 1 / 32), rt_fn, reps=8))
+
+    legs = [l for l in legs if wanted(l.name)]
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+
+    for s in range(args.warmup):
+        for leg in legs:
+            leg.run(s)
+    torch.cuda.synchronize()
+
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in legs]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for j, leg in enumerate(legs):
+            evs[s][j][0].record(stream)
+            leg.run(args.warmup + s)
+            evs[s][j][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for s in range(args.steps):
+        for j, leg in enumerate(legs):
+            leg.ms += evs[s][j][0].elapsed_time(evs[s][j][1])
+
+    K = args.steps
+    out_legs = []
+    for leg in legs:
+        per_call_ms = leg.ms / (K * leg.reps)
+        d = {"name": leg.name, "kernel": leg.kernel, "us": round(per_call_ms * 1e3, 2)}
+        if leg.kind == "flop":
+            rate = leg.work / (per_call_ms * 1e-3) / 1e12
+            d.update({"tflop": round(leg.work / 1e12, 4), "TFLOP/s": round(rate, 1),
+                      "frac_mfma": round(rate / MFMA_BF16_PEAK_TFLOPS, 4)})
+        else:
+            rate = leg.work / (per_call_ms * 1e-3) / 1e9
+            d.update({"GB": round(leg.work / 1e9, 4), "GB/s": round(rate, 1), "frac_hbm": round(rate / HBM_PEAK_GBPS, 4)})
+        out_legs.append(d)
+
+    moe_legs = [l for l in legs if l.name.startswith("moe.")]
+    moe_rows = int(moe["counts"].sum()) if moe is not None else 0
+    moe_flop = sum(l.work for l in moe_legs)
+    moe_ms = sum(l.ms for l in moe_legs) / K
+    value = moe_flop / (moe_ms * 1e-3) / 1e12 if moe_ms > 0 else None
+    codec = [l for l in legs if l.kind == "byte" and not l.name.startswith("roundtrip")]
+    codec_bytes = sum(l.work * l.reps for l in codec)
+    codec_ms = sum(l.ms for l in codec) / K
+    hbm_gbps = codec_bytes / (codec_ms * 1e-3) / 1e9 if codec_ms > 0 else None
+
+    # dominant kernel: the instantiation with the largest total event time
+    by_kernel = {}
+    for l in legs:
+        b = by_kernel.setdefault(l.kernel, {"ms": 0.0, "work": 0.0, "launches": 0, "kind": l.kind})
+        b["ms"] += l.ms / K
+        b["work"] += l.work * l.reps
+        b["launches"] += l.reps
+    dom_name, dom = max(by_kernel.items(), key=lambda kv: kv[1]["ms"])
+    avg_launch_ms = dom["ms"] / dom["launches"]
+    work_per_launch = dom["work"] / dom["launches"]
+    if dom["kind"] == "flop":
+        achieved, peak, unit, bound = work_per_launch / (avg_launch_ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = work_per_launch / (avg_launch_ms * 1e-3) / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
+    roofline = {"bound": bound, "kernel": dom_name, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "avg_launch_us": round(avg_launch_ms * 1e3, 1),
+                "work_per_launch": work_per_launch, "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline and moe is not None:
+        cpu = cpu_baseline(moe)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1) if value else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; synth/)",
+        "config": {
+            "workload": "routed-expert layer share (32 experts, hidden 7168, intermediate 2048, 131072 routed rows, "
+                        "fwd + grad_x) + 8-expert GEMM [4096x4096 -> 2048] + bf16 KV cache [4,8192,512] fake-quant "
+                        "fp8/128, mxfp4/32, nvfp4/16 + STE + bulk bf16 [65536,7168] codecs + [64,4096,4096] weight dequant",
+            "value_is": "grouped-GEMM TFLOP/s of the routed-expert layer legs (event time)",
+            "moe_rows": moe_rows,
+        },
+        "hbm": {"GB/s": round(hbm_gbps, 1) if hbm_gbps else None,
+                "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4) if hbm_gbps else None,
+                "legs": "codec legs: kv + bulk"},
+        "mfma": {"TFLOP/s": round(value, 1) if value else None,
+                 "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4) if value else None},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "legs": out_legs,
+        "setup_s": round(t_gen, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(moe):
+    """The oracle (float64 NumPy, unmodified) on a bounded sample of the
+    routed-expert layer: gate/up forward of 1024 rows in each of 6 experts."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                           default=1)
+    except Exception:
+        blas_threads = None
+    offs = moe["offs"]
+    starts = np.concatenate([[0], offs[:-1]])
+    experts = [e for e in range(len(offs)) if offs[e] - starts[e] >= 1024][:6]
+    rows = np.concatenate([np.arange(starts[e], starts[e] + 1024) for e in experts])
+    x_rows = oracle.from_dtype_bits(moe["tokens_x"][moe["row_token"][rows]], "bf16")
+    t0 = time.perf_counter()
+    y, _ = oracle.grouped_mm_rows(rows, moe["gu_packed"], moe["gu_scales"], offs, x_rows=x_rows)
+    dt = time.perf_counter() - t0
+    flop = 2.0 * len(rows) * moe["gu_packed"].shape[1] * moe["gu_packed"].shape[2] * 2
+    return {"value": round(flop / dt / 1e12, 4), "unit": "TFLOP/s", "cores": blas_threads,
+            "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"gate/up forward, 1024 rows x {len(experts)} experts (float64 dequant + BLAS matmul), "
+                      f"{flop / 1e9:.0f} GFLOP in {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
