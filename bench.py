@@ -78,8 +78,8 @@ def main():
     sp = stream.cuda_stream
     want = None if args.legs == "all" else [p.strip() for p in args.legs.split(",")]
 
-    def wanted(name):
-        return want is None or any(name.startswith(p) for p in want)
+    def wanted(name):   # a leg (or a group prefix of legs) asked for by --legs
+        return want is None or any(name.startswith(p) or p.startswith(name) for p in want)
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)

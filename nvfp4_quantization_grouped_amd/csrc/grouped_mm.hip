@@ -64,6 +64,10 @@ __device__ __forceinline__ TileInfo find_tile(const int32_t* __restrict__ offs, 
   return TileInfo{0, 0, -2};
 }
 
+__device__ __forceinline__ const uint8_t* packed_e_of(const uint8_t* packed, int e, int64_t ndim, int64_t kdim) {
+  return packed + (int64_t)e * ndim * (kdim / 2);
+}
+
 template <int BM, int BN>
 struct GemmLds {
   uint8_t a[2][BM * kLdsRow];
@@ -301,6 +305,322 @@ k_grouped_mm(const uint8_t* __restrict__ a,        // x [T, red] (fwd) or grad_o
   }
 }
 
+// ---------------------------------------------------------- forward, v2
+// Forward with the weight operand kept out of LDS.  The workgroup owns a
+// 128 x 256 output tile; its 4 waves split the columns (wave tile 128 x 64,
+// 4 x 2 MFMA tiles).  Within a reduction step of 64, lane-half h takes the
+// 32 consecutive k [k0 + 32h, k0 + 32h + 32) -- one E8M0 scale block -- and
+// sub-step kk the 8 values k0 + 32h + 8kk .. +7; A and B use the same
+// assignment, so the sum is unchanged.  A lane therefore fetches its weight
+// row's 16 packed bytes and one scale byte per column tile and step straight
+// from global memory and decodes them into its four B fragments; only the
+// activation tile goes through (double-buffered) LDS.  37 KB of LDS and
+// <= 256 registers per lane let two workgroups share a CU.
+constexpr int kFwdBM = 128, kFwdBN = 256;
+
+__global__ void __launch_bounds__(kGemmThreads, 2)
+k_grouped_mm_fwd(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
+                 const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
+                 int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out) {
+  constexpr int BM = kFwdBM, BN = kFwdBN, MT = BM / 32, NT = BN / 4 / 32;
+  const int64_t col0 = (int64_t)blockIdx.x * BN;
+  const TileInfo ti = find_tile<BM>(offs, experts, tokens, blockIdx.y);
+  if (ti.expert == -2) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, r = lane & 31;
+
+  if (ti.expert == -1) {
+    for (int i = threadIdx.x; i < BM * BN / 8; i += kGemmThreads) {
+      const int rr = i / (BN / 8), c = (i % (BN / 8)) * 8;
+      const int64_t gr = ti.row0 + rr, gc = col0 + c;
+      if (gr < ti.row_end && gc < ndim) {
+        unsigned short* dst = reinterpret_cast<unsigned short*>(out + (gr * ndim + gc) * 2);
+        for (int q = 0; q < 8 && gc + q < ndim; ++q) dst[q] = 0;
+      }
+    }
+    return;
+  }
+
+  __shared__ uint8_t lds_a[2][BM * kLdsRow];
+  const uint8_t* packed_e = packed + (int64_t)ti.expert * ndim * (kdim / 2);
+  const uint8_t* scales_e = scales + (int64_t)ti.expert * ndim * (kdim / 32);
+
+  ALoader<BM> al;
+  // this lane's weight rows (one per column tile) and their validity
+  int64_t wrow[NT];
+  bool wok[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    wrow[j] = col0 + wave * (BN / 4) + j * 32 + r;
+    wok[j] = wrow[j] < ndim;
+  }
+  u32x4_t pb[NT];
+  uint32_t sb[NT];
+  auto load_b = [&](int64_t k0) {
+    const int64_t kb = k0 + 32 * h;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      if (wok[j] && kb < kdim) {
+        pb[j] = *reinterpret_cast<const u32x4_t*>(packed_e + wrow[j] * (kdim / 2) + kb / 2);
+        sb[j] = scales_e[wrow[j] * (kdim / 32) + kb / 32];
+      } else {
+        pb[j] = u32x4_t{0u, 0u, 0u, 0u};
+        sb[j] = 127u;
+      }
+    }
+  };
+
+  f32x16_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x16_t{};
+
+  const int nsteps = (int)((kdim + kBK - 1) / kBK);
+  al.load(a, kdim, ti.row0, ti.row_end, 0, kdim);
+  load_b(0);
+  al.store(lds_a[0]);
+  __syncthreads();
+
+  for (int s = 0; s < nsteps; ++s) {
+    const int cur = s & 1;
+    // decode this step's weights into B fragments
+    bf16x8_t fb[NT][4];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const float sc = e8m0_to_f32(sb[j]);
+      const uint32_t w[4] = {pb[j].x, pb[j].y, pb[j].z, pb[j].w};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        u32x4_t v = {dec_fp4_bf16x2<0>(w[kk], sc), dec_fp4_bf16x2<1>(w[kk], sc), dec_fp4_bf16x2<2>(w[kk], sc),
+                     dec_fp4_bf16x2<3>(w[kk], sc)};
+        fb[j][kk] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+    if (s + 1 < nsteps) {
+      al.load(a, kdim, ti.row0, ti.row_end, (int64_t)(s + 1) * kBK, kdim);
+      load_b((int64_t)(s + 1) * kBK);
+    }
+    const uint8_t* la = lds_a[cur] + r * kLdsRow + 64 * h;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8_t fa[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(la + i * 32 * kLdsRow + kk * 16);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j][kk], acc[i][j], 0, 0, 0);
+    }
+    if (s + 1 < nsteps) al.store(lds_a[cur ^ 1]);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int64_t gc = wrow[j];
+#pragma unroll
+      for (int q = 0; q < 16; q += 2) {
+        const int64_t gr0 = ti.row0 + i * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
+        f32x2_t v = {acc[i][j][q], acc[i][j][q + 1]};
+        const uint32_t bb = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+        if (wok[j]) {
+          if (gr0 < ti.row_end) *reinterpret_cast<unsigned short*>(out + (gr0 * ndim + gc) * 2) = (unsigned short)(bb & 0xFFFFu);
+          if (gr0 + 1 < ti.row_end) *reinterpret_cast<unsigned short*>(out + ((gr0 + 1) * ndim + gc) * 2) = (unsigned short)(bb >> 16);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------- forward, v3
+// Same tile and fragment scheme as v2, but every global transfer of the main
+// loop is a direct global->LDS DMA (global_load_lds_*), issued two steps
+// ahead into a ring of three LDS stages:
+//  * activations: the 128 x 64 bf16 tile (16 KB) as 16 blocks of 1 KB; a
+//    block holds 8 rows, and within a row the eight 16-byte chunks are
+//    XOR-swizzled by ((row >> 1) & 7): LDS serves 16 lanes x 16 bytes (256
+//    bytes, two 128-byte rows) per cycle, and with this swizzle any 16
+//    consecutive rows read at one logical chunk hit 16 distinct 16-byte bank
+//    groups, so the fragment reads are conflict-free without padding;
+//  * weights: each wave fetches the packed bytes of its own 64 weight rows
+//    (2 blocks of 1 KB, laid out [row/32][half][row%32] x 16 bytes, so a
+//    lane's 16 bytes -- one 32-k scale block -- sit next to its neighbours')
+//    and their scale bytes (the aligned dword holding this step's two
+//    32-k blocks and the neighbouring step's, 4 bytes per lane);
+//  * each step waits for exactly the DMA of the step it is about to use
+//    (s_waitcnt vmcnt(N), N = operations issued after it), then barriers.
+// With no register-destined loads in the loop, no other waits are needed.
+// The step index of the prefetch is clamped at the end, so every iteration
+// issues the same operations (keeping N constant); the surplus transfers are
+// in-bounds and land in a stage nobody reads.  Rows past the expert's segment
+// load a clamped valid row and are never stored; weight rows past N
+// likewise.  Needs K % 128 == 0 (4-byte aligned scale rows).
+constexpr int kV3Stages = 3;
+constexpr int kV3ABytes = kFwdBM * 128;          // 16 KB, unpadded (swizzled)
+constexpr int kV3BBytes = kFwdBN * 32;           // 8 KB packed weights
+constexpr int kV3SBytes = kFwdBN * 4;            // 1 KB scales (4 bytes = 2 steps per row)
+constexpr int kV3DmaPerStep = 4 + 2 + 1;         // per wave: A, packed B, scales
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt immediate: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits
+  // 15:14, expcnt bits 6:4 (left at its maximum), lgkmcnt bits 11:8 = 0:
+  // this wave's LDS reads of the stage are complete before anyone passes the
+  // barrier and starts refilling it.
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70);
+  asm volatile("s_barrier" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+struct V3Stage {
+  uint8_t a[kV3ABytes];
+  uint8_t b[kV3BBytes];
+  uint8_t s[kV3SBytes];
+};
+
+__global__ void __launch_bounds__(kGemmThreads, 2)
+k_grouped_mm_fwd_v3(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
+                    const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
+                    int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out) {
+  constexpr int BM = kFwdBM, BN = kFwdBN, MT = BM / 32, NT = BN / 4 / 32;
+  const int64_t col0 = (int64_t)blockIdx.x * BN;
+  const TileInfo ti = find_tile<BM>(offs, experts, tokens, blockIdx.y);
+  if (ti.expert == -2) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, r = lane & 31;
+
+  if (ti.expert == -1) {
+    for (int i = threadIdx.x; i < BM * BN / 8; i += kGemmThreads) {
+      const int rr = i / (BN / 8), c = (i % (BN / 8)) * 8;
+      const int64_t gr = ti.row0 + rr, gc = col0 + c;
+      if (gr < ti.row_end && gc < ndim) {
+        unsigned short* dst = reinterpret_cast<unsigned short*>(out + (gr * ndim + gc) * 2);
+        for (int q = 0; q < 8 && gc + q < ndim; ++q) dst[q] = 0;
+      }
+    }
+    return;
+  }
+
+  __shared__ __attribute__((aligned(1024))) V3Stage st[kV3Stages];
+
+  // activation DMA: this wave fills A blocks 4*wave .. 4*wave+3; block b holds
+  // rows 8b .. 8b+7: lane l -> row 8b + l/8, LDS chunk l%8 <- global chunk
+  // (l%8) ^ ((row >> 1) & 7)
+  const uint8_t* a_src[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = 8 * (4 * wave + q) + (lane >> 3);
+    int64_t grow = ti.row0 + row;
+    if (grow >= ti.row_end) grow = ti.row_end - 1;
+    a_src[q] = a + (grow * kdim + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2;
+  }
+  // weight DMA: this wave's rows n = col0 + 64*wave + 32*j + r (j = 0, 1);
+  // block j holds [half h][row r] x 16 bytes; scales: 2 bytes per row
+  const uint8_t* packed_e = packed_e_of(packed, ti.expert, ndim, kdim);
+  const uint8_t* b_src[NT];
+  bool wok[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    int64_t n = col0 + wave * (BN / 4) + j * 32 + r;
+    wok[j] = n < ndim;
+    if (!wok[j]) n = ndim - 1;
+    b_src[j] = packed_e + n * (kdim / 2) + 16 * h;
+  }
+  int64_t n_s = col0 + wave * (BN / 4) + lane;
+  if (n_s >= ndim) n_s = ndim - 1;
+  const uint8_t* s_src = scales + ((int64_t)ti.expert * ndim + n_s) * (kdim / 32);   // 4-byte aligned: K % 128 == 0
+
+  auto dma_step = [&](int step, int stage) {
+    V3Stage& d = st[stage];
+    const int64_t ka = (int64_t)step * kBK * 2;     // activation bytes
+    const int64_t kb = (int64_t)step * 32;          // packed bytes
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_global_load_lds(a_src[q] + ka, (lds_void_t*)(d.a + 4096 * wave + 1024 * q), 16, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      __builtin_amdgcn_global_load_lds(b_src[j] + kb, (lds_void_t*)(d.b + 2048 * wave + 1024 * j), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(s_src + 4 * (step >> 1), (lds_void_t*)(d.s + 256 * wave), 4, 0, 0);
+  };
+
+  f32x16_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x16_t{};
+
+  const int nsteps = (int)(kdim / kBK);
+  const int last = nsteps - 1;
+  dma_step(0, 0);
+  dma_step(min(1, last), 1);
+  wait_vmcnt_barrier<kV3DmaPerStep>();          // step 0 landed; step 1 may be in flight
+
+  const int swz_base = r * 128;
+  int stage = 0;
+  for (int s = 0; s < nsteps; ++s) {
+    __builtin_amdgcn_sched_barrier(0);
+    dma_step(min(s + 2, last), stage == 0 ? 2 : stage - 1);   // stage (s+2) % 3
+    const V3Stage& c = st[stage];
+    // decode this wave's weights for the step into B fragments
+    bf16x8_t fb[NT][4];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const u32x4_t p = *reinterpret_cast<const u32x4_t*>(c.b + 2048 * wave + 1024 * j + 512 * h + 16 * r);
+      const float sc = e8m0_to_f32(c.s[4 * (wave * 64 + j * 32 + r) + 2 * (s & 1) + h]);
+      const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        u32x4_t v = {dec_fp4_bf16x2<0>(w[kk], sc), dec_fp4_bf16x2<1>(w[kk], sc), dec_fp4_bf16x2<2>(w[kk], sc),
+                     dec_fp4_bf16x2<3>(w[kk], sc)};
+        fb[j][kk] = __builtin_bit_cast(bf16x8_t, v);
+      }
+    }
+    const uint8_t* la = c.a + swz_base;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int off = 16 * ((4 * h + kk) ^ ((r >> 1) & 7));   // rows 32i + r share the swizzle
+      bf16x8_t fa[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(la + i * 32 * 128 + off);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j][kk], acc[i][j], 0, 0, 0);
+    }
+    // step s+1 has landed once only the DMA of step s+2 may be in flight
+    wait_vmcnt_barrier<kV3DmaPerStep>();
+    __builtin_amdgcn_sched_barrier(0);
+    stage = stage == kV3Stages - 1 ? 0 : stage + 1;
+  }
+  // drain the clamped tail transfers before this workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
+
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int64_t gc = col0 + wave * (BN / 4) + j * 32 + r;
+#pragma unroll
+      for (int q = 0; q < 16; q += 2) {
+        const int64_t gr0 = ti.row0 + i * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
+        f32x2_t v = {acc[i][j][q], acc[i][j][q + 1]};
+        const uint32_t bb = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+        if (wok[j]) {
+          if (gr0 < ti.row_end) *reinterpret_cast<unsigned short*>(out + (gr0 * ndim + gc) * 2) = (unsigned short)(bb & 0xFFFFu);
+          if (gr0 + 1 < ti.row_end) *reinterpret_cast<unsigned short*>(out + ((gr0 + 1) * ndim + gc) * 2) = (unsigned short)(bb >> 16);
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launcher
 template <int BM, int BN, bool BWD>
 static hipError_t launch_t(const void* a, int64_t tokens, const int8_t* packed, const uint8_t* scales,
@@ -318,15 +638,26 @@ static hipError_t launch_t(const void* a, int64_t tokens, const int8_t* packed, 
 hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8_t* packed, const uint8_t* scales,
                              int64_t experts, int64_t wn_dim, int64_t wk_dim, const int32_t* offs, void* out,
                              hipStream_t st) {
-  // Column tile: 256 when the output is wide, 128 otherwise (more tiles for small problems).
-  const int64_t cols = bwd ? wk_dim : wn_dim;
-  const int64_t tiles256 = ((tokens + 255) / 256 + experts) * ((cols + 255) / 256);
-  if (tiles256 >= 1024) {
-    return bwd ? launch_t<256, 256, true>(a, tokens, packed, scales, experts, wn_dim, wk_dim, offs, out, st)
-               : launch_t<256, 256, false>(a, tokens, packed, scales, experts, wn_dim, wk_dim, offs, out, st);
+  if (!bwd) {
+    const int64_t gx = (wn_dim + kFwdBN - 1) / kFwdBN;
+    const int64_t gy = (tokens + kFwdBM - 1) / kFwdBM + experts;
+    if (wk_dim % 128 == 0 && ((uintptr_t)scales & 3) == 0) {
+      hipLaunchKernelGGL(k_grouped_mm_fwd_v3, dim3((unsigned)gx, (unsigned)gy), dim3(kGemmThreads), 0, st,
+                         (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim,
+                         wk_dim, (uint8_t*)out);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL(k_grouped_mm_fwd, dim3((unsigned)gx, (unsigned)gy), dim3(kGemmThreads), 0, st,
+                       (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim,
+                       (uint8_t*)out);
+    return hipGetLastError();
   }
-  return bwd ? launch_t<256, 128, true>(a, tokens, packed, scales, experts, wn_dim, wk_dim, offs, out, st)
-             : launch_t<256, 128, false>(a, tokens, packed, scales, experts, wn_dim, wk_dim, offs, out, st);
+  // Column tile: 256 when the output is wide, 128 otherwise (more tiles for small problems).
+  const int64_t cols = wk_dim;
+  const int64_t tiles256 = ((tokens + 255) / 256 + experts) * ((cols + 255) / 256);
+  if (tiles256 >= 1024)
+    return launch_t<256, 256, true>(a, tokens, packed, scales, experts, wn_dim, wk_dim, offs, out, st);
+  return launch_t<256, 128, true>(a, tokens, packed, scales, experts, wn_dim, wk_dim, offs, out, st);
 }
 
 }  // namespace mxq
