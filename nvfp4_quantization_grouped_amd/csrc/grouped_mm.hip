@@ -621,6 +621,179 @@ k_grouped_mm_fwd_v3(const uint8_t* __restrict__ a, const uint8_t* __restrict__ p
   }
 }
 
+// ----------------------------------------------------------- backward, v2
+// grad_x = grad_out @ W_e.  Tile: 128 token rows x 256 output columns (k),
+// reduction over n in steps of 64; 4 waves split the columns (wave tile
+// 128 x 64), two workgroups per CU.
+//  * grad_out tile (128 x 64 bf16) is staged through registers into a
+//    double-buffered LDS tile (same (row >> 1) & 7 chunk swizzle as the
+//    forward), loaded one step ahead;
+//  * weights: each wave builds a private transposed tile Wt[k][n] of its
+//    64 columns x 64 n in LDS.  Lane (nb, kb) = (lane % 8, lane / 8) owns the
+//    8 x 8 block n = 8nb.., k = 64*wave + 8kb..: it loads 8 packed dwords and
+//    the 8 rows' scale bytes one step ahead, decodes them (scaled fp4 ->
+//    bf16), regroups the 8 x 8 block with v_perm into 8 rows of 8 n-values and
+//    writes them to Wt, which only its own wave reads (no barrier needed);
+//  * MFMA fragments as in the forward: lane-half h covers n in
+//    [32h, 32h + 32) of the step, sub-step kk the 8 values 32h + 8kk ..
+constexpr int kBwdBM = 128, kBwdBN = 256;
+
+__global__ void __launch_bounds__(kGemmThreads, 2)
+k_grouped_mm_bwd_v2(const uint8_t* __restrict__ g, const uint8_t* __restrict__ packed,
+                    const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
+                    int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out) {
+  constexpr int BM = kBwdBM, BN = kBwdBN, MT = BM / 32, NT = BN / 4 / 32;
+  const int64_t col0 = (int64_t)blockIdx.x * BN;
+  const TileInfo ti = find_tile<BM>(offs, experts, tokens, blockIdx.y);
+  if (ti.expert == -2) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, r = lane & 31;
+
+  if (ti.expert == -1) {
+    for (int i = threadIdx.x; i < BM * BN / 8; i += kGemmThreads) {
+      const int rr = i / (BN / 8), c = (i % (BN / 8)) * 8;
+      const int64_t gr = ti.row0 + rr, gc = col0 + c;
+      if (gr < ti.row_end && gc < kdim) {
+        unsigned short* dst = reinterpret_cast<unsigned short*>(out + (gr * kdim + gc) * 2);
+        for (int q = 0; q < 8 && gc + q < kdim; ++q) dst[q] = 0;
+      }
+    }
+    return;
+  }
+
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_g[2][BM * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_wt[4][64 * 128];
+
+  // grad_out staging: thread t owns chunks c = t + 256 i: row c / 8, chunk c % 8
+  u32x4_t gr_regs[4];
+  auto load_g = [&](int64_t n0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = threadIdx.x + i * kGemmThreads;
+      const int64_t row = ti.row0 + (c >> 3), n = n0 + (c & 7) * 8;
+      if (row < ti.row_end && n < ndim)
+        gr_regs[i] = *reinterpret_cast<const u32x4_t*>(g + (row * ndim + n) * 2);
+      else
+        gr_regs[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_g = [&](uint8_t* dst) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = threadIdx.x + i * kGemmThreads;
+      const int row = c >> 3, chunk = c & 7;
+      *reinterpret_cast<u32x4_t*>(dst + row * 128 + 16 * (chunk ^ ((row >> 1) & 7))) = gr_regs[i];
+    }
+  };
+
+  // weight block of this lane: rows n0 + 8nb + i (i < 8), columns kcol .. kcol+7
+  const int nb = lane & 7, kb = lane >> 3;
+  const int64_t kcol = col0 + wave * 64 + kb * 8;
+  const bool kok = kcol < kdim;
+  const int64_t prow = kdim / 2, srow = kdim / 32;     // bytes per weight row (packed, scales)
+  const uint8_t* pbase = packed_e_of(packed, ti.expert, ndim, kdim) + (int64_t)nb * 8 * prow + kcol / 2;
+  const uint8_t* sbase = scales + (int64_t)ti.expert * ndim * srow + (int64_t)nb * 8 * srow + kcol / 32;
+  uint32_t pw[8], sw[8];
+  auto load_w = [&](int64_t n0) {
+    const uint8_t* pp = pbase + n0 * prow;
+    const uint8_t* sp = sbase + n0 * srow;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (kok && n0 + nb * 8 + i < ndim) {
+        pw[i] = *reinterpret_cast<const uint32_t*>(pp + i * prow);
+        sw[i] = sp[i * srow];
+      } else {
+        pw[i] = 0u;
+        sw[i] = 127u;
+      }
+    }
+  };
+  uint8_t* wt = lds_wt[wave];
+  auto build_wt = [&]() {
+    // two halves of 4 rows: decode, then regroup each output row's 4 n-values
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t d[4][4];   // d[row][pair q]: bf16 of k = 2q (lo), 2q+1 (hi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sc = e8m0_to_f32(sw[4 * half + i]);
+        const uint32_t p = pw[4 * half + i];
+        d[i][0] = dec_fp4_bf16x2<0>(p, sc);
+        d[i][1] = dec_fp4_bf16x2<1>(p, sc);
+        d[i][2] = dec_fp4_bf16x2<2>(p, sc);
+        d[i][3] = dec_fp4_bf16x2<3>(p, sc);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {   // Wt row k = 8kb + j, logical chunk nb, 8-byte half `half`
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        u32x2_t o;
+        o.x = __builtin_amdgcn_perm(d[1][j >> 1], d[0][j >> 1], sel);
+        o.y = __builtin_amdgcn_perm(d[3][j >> 1], d[2][j >> 1], sel);
+        const int k = kb * 8 + j;
+        *reinterpret_cast<u32x2_t*>(wt + k * 128 + 16 * (nb ^ ((k >> 1) & 7)) + 8 * half) = o;
+      }
+    }
+  };
+
+  f32x16_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x16_t{};
+
+  const int nsteps = (int)((ndim + kBK - 1) / kBK);
+  load_g(0);
+  load_w(0);
+  store_g(lds_g[0]);
+  __syncthreads();
+
+  const int swz = (r >> 1) & 7;
+  for (int s = 0; s < nsteps; ++s) {
+    const int cur = s & 1;
+    build_wt();                                   // this step's weights -> this wave's Wt
+    if (s + 1 < nsteps) {
+      load_g((int64_t)(s + 1) * kBK);
+      load_w((int64_t)(s + 1) * kBK);
+    }
+    const uint8_t* la = lds_g[cur] + r * 128;
+    const uint8_t* lb = wt + r * 128;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int off = 16 * ((4 * h + kk) ^ swz);
+      bf16x8_t fa[MT], fb[NT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(la + i * 32 * 128 + off);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) fb[j] = *reinterpret_cast<const bf16x8_t*>(lb + j * 32 * 128 + off);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (s + 1 < nsteps) store_g(lds_g[cur ^ 1]);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int64_t gc = col0 + wave * (BN / 4) + j * 32 + r;
+#pragma unroll
+      for (int q = 0; q < 16; q += 2) {
+        const int64_t gr0 = ti.row0 + i * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
+        f32x2_t v = {acc[i][j][q], acc[i][j][q + 1]};
+        const uint32_t bb = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+        if (gc < kdim) {
+          if (gr0 < ti.row_end) *reinterpret_cast<unsigned short*>(out + (gr0 * kdim + gc) * 2) = (unsigned short)(bb & 0xFFFFu);
+          if (gr0 + 1 < ti.row_end) *reinterpret_cast<unsigned short*>(out + ((gr0 + 1) * kdim + gc) * 2) = (unsigned short)(bb >> 16);
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launcher
 template <int BM, int BN, bool BWD>
 static hipError_t launch_t(const void* a, int64_t tokens, const int8_t* packed, const uint8_t* scales,
@@ -648,6 +821,14 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
       return hipGetLastError();
     }
     hipLaunchKernelGGL(k_grouped_mm_fwd, dim3((unsigned)gx, (unsigned)gy), dim3(kGemmThreads), 0, st,
+                       (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim,
+                       (uint8_t*)out);
+    return hipGetLastError();
+  }
+  {
+    const int64_t gx = (wk_dim + kBwdBN - 1) / kBwdBN;
+    const int64_t gy = (tokens + kBwdBM - 1) / kBwdBM + experts;
+    hipLaunchKernelGGL(k_grouped_mm_bwd_v2, dim3((unsigned)gx, (unsigned)gy), dim3(kGemmThreads), 0, st,
                        (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim,
                        (uint8_t*)out);
     return hipGetLastError();
