@@ -118,10 +118,10 @@ def main():
                                                             offs.data_ptr(), gx.data_ptr(), sp), "bwd_x")
 
         legs += [
-            Leg("moe.gate_up.fwd", "k_grouped_mm<256,256,fwd>", "flop", 2.0 * moe_rows * I2 * H, fwd(x_routed, gu_p, gu_s, I2, H, gu_y)),
-            Leg("moe.down.fwd", "k_grouped_mm<256,256,fwd>", "flop", 2.0 * moe_rows * H * I, fwd(h, dn_p, dn_s, H, I, dn_y)),
-            Leg("moe.down.bwd_x", "k_grouped_mm<256,256,bwd>", "flop", 2.0 * moe_rows * H * I, bwd(dn_g, dn_p, dn_s, H, I, dn_gx)),
-            Leg("moe.gate_up.bwd_x", "k_grouped_mm<256,256,bwd>", "flop", 2.0 * moe_rows * I2 * H, bwd(gu_g, gu_p, gu_s, I2, H, gu_gx)),
+            Leg("moe.gate_up.fwd", "k_grouped_mm_fwd_dma", "flop", 2.0 * moe_rows * I2 * H, fwd(x_routed, gu_p, gu_s, I2, H, gu_y)),
+            Leg("moe.down.fwd", "k_grouped_mm_fwd_dma", "flop", 2.0 * moe_rows * H * I, fwd(h, dn_p, dn_s, H, I, dn_y)),
+            Leg("moe.down.bwd_x", "k_grouped_mm_bwd", "flop", 2.0 * moe_rows * H * I, bwd(dn_g, dn_p, dn_s, H, I, dn_gx)),
+            Leg("moe.gate_up.bwd_x", "k_grouped_mm_bwd", "flop", 2.0 * moe_rows * I2 * H, bwd(gu_g, gu_p, gu_s, I2, H, gu_gx)),
         ]
 
     # ---------------- 8-expert grouped GEMM forward (4 rotating buffer sets > 256 MB)
@@ -138,7 +138,7 @@ def main():
             j = i % R8
             check(L.mxfp4_grouped_mm_fwd(e8_x[j].data_ptr(), 4096, 4096, e8_p[j].data_ptr(), e8_s[j].data_ptr(), 8,
                                          2048, e8_o.data_ptr(), e8_y[j].data_ptr(), sp), "e8 fwd")
-        legs.append(Leg("e8.fwd", "k_grouped_mm<256,128,fwd>", "flop", 2.0 * 4096 * 2048 * 4096, e8_fn, reps=R8))
+        legs.append(Leg("e8.fwd", "k_grouped_mm_fwd_dma", "flop", 2.0 * 4096 * 2048 * 4096, e8_fn, reps=R8))
 
     # ---------------- KV cache quantize_cache x3 + STE (8 rotating sets: 8 x 64 MiB per leg)
     if wanted("kv"):
@@ -267,7 +267,7 @@ def main():
         achieved, peak, unit, bound = work_per_launch / (avg_launch_ms * 1e-3) / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
     roofline = {"bound": bound, "kernel": dom_name, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "avg_launch_us": round(avg_launch_ms * 1e3, 1),
-                "work_per_launch": work_per_launch, "traffic": None}
+                "work_per_launch": work_per_launch, "traffic": measured_traffic(dom_name)}
 
     cpu = None
     if not args.no_cpu_baseline and moe is not None:
@@ -304,6 +304,28 @@ def main():
         "setup_s": round(t_gen, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(kernel):
+    """HBM-side bytes per launch of `kernel` from the committed counter summary
+    (rocprofv3 FETCH_SIZE and WRITE_SIZE, calibrated on the copy kernel), or
+    None when there is none or the kernel source changed since it was taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    with open(os.path.join(here, k["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != k["source_sha256"]:
+            return None
+    return {"bytes_per_launch": k["bytes_per_launch"], "fetch_bytes": k["fetch_bytes"],
+            "write_bytes": k["write_bytes"], "calibration": rec.get("calibration"), "from": "profiles/traffic.json"}
 
 
 def cpu_baseline(moe):

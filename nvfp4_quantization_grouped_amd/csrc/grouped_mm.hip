@@ -3,28 +3,30 @@
 //   forward   y[rows_e]      = x[rows_e]        @ W_e^T     (reduce over k)
 //   backward  grad_x[rows_e] = grad_out[rows_e] @ W_e       (reduce over n)
 // with W_e [n, k] stored as mxfp4 (packed [E, n, k/2] + E8M0 scales
-// [E, n, k/32]) and dequantized on the fly: packed bytes go HBM -> registers,
-// are decoded to bf16 with gfx950's scaled fp4 conversion and written to LDS,
-// from where the bf16 MFMA (v_mfma_f32_32x32x16_bf16) reads them.  The bf16
-// weight never exists in HBM.  Accumulation is fp32, output bf16 nearest-even.
+// [E, n, k/32]) and dequantized on the fly with gfx950's scaled fp4
+// conversion straight into bf16 MFMA operands (v_mfma_f32_32x32x16_bf16).
+// The bf16 weight never exists in HBM.  fp32 accumulation, bf16
+// nearest-even output.
 //
-// Tiling: a workgroup of 4 waves owns a BM x BN output tile; wave (wm, wn)
-// owns (BM/2) x (BN/2) of it as a grid of 32x32 MFMA tiles.  The reduction
-// runs in steps of 64 through two LDS stages: while the MFMAs consume one
-// stage, the next step's global loads are in flight and are then written
-// (and, for weights, decoded) into the other stage.  LDS rows are padded to
-// 144 bytes so the 16-byte fragment reads of 32 consecutive rows hit
-// distinct banks.
+// All kernels: 256 threads (4 waves) own a 128-row x 256-column output tile;
+// the waves split the columns (wave tile 128 x 64 = 4 x 2 MFMA tiles, 128
+// fp32 accumulators per lane), and two workgroups share a CU so one's
+// memory phase overlaps the other's MFMAs.  The reduction runs in steps of
+// 64, and inside a step lane-half h of a wave covers the 32 consecutive
+// reduction indices [32h, 32h + 32) -- for the forward exactly one E8M0
+// scale block -- with sub-step kk taking the 8 values 32h + 8kk ..; both
+// operands use the same assignment, so the sum is unchanged.
 //
 // Scheduling: grid.x walks output-column tiles, grid.y walks "row-tile
 // slots".  Each workgroup reads the device offsets and finds which expert
 // and which row tile of it its slot is (sum over experts of
-// ceil(rows_e / BM) <= ceil(T / BM) + E slots are launched).  Slots past the
-// last tile zero the rows no expert owns.  No host synchronization.
-//
-// Backward: the reduction index is n, but W_e is contiguous along k, so the
-// weight tile is transposed while it is decoded: a thread decodes an 8 x 8
-// (n x k) block and regroups it with v_perm into 8 rows of 8 n-values.
+// ceil(rows_e / 128) <= ceil(T / 128) + E slots are launched).  Slots past
+// the last tile zero the rows no expert owns.  No host synchronization.
+// With the default round-robin dispatch of workgroups over the 8 XCDs,
+// column tile x runs on XCD x % 8 for every row slot, so each XCD's L2 keeps
+// the same weight columns hot while the activation blocks it shares with the
+// other XCDs are served from the Infinity Cache (this measured faster than
+// giving each XCD a contiguous range of row slots).
 #include <type_traits>
 
 #include "launch.hpp"
@@ -68,12 +70,6 @@ __device__ __forceinline__ const uint8_t* packed_e_of(const uint8_t* packed, int
   return packed + (int64_t)e * ndim * (kdim / 2);
 }
 
-template <int BM, int BN>
-struct GemmLds {
-  uint8_t a[2][BM * kLdsRow];
-  uint8_t b[2][BN * kLdsRow];
-};
-
 // ---------------------------------------------------------------- A operand
 // A tile: BM rows x 64 bf16 of a row-major [rows, ld] bf16 matrix.
 template <int BM>
@@ -104,209 +100,8 @@ struct ALoader {
   }
 };
 
-// ------------------------------------------------------- B operand, forward
-// Weight tile for y = x W^T: BN weight rows (n) x 64 k.  A thread owns
-// 32/TPR consecutive k of one row: 16 or 32 packed bytes, 1 or 2 scales.
-template <int BN>
-struct BFwdLoader {
-  static constexpr int kTPR = kGemmThreads / BN;       // threads per weight row (1 or 2)
-  static constexpr int kVec = 2 / kTPR;                // 16-byte packed loads per thread
-  u32x4_t p[kVec];
-  uint32_t sb[kVec];
-
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ packed_e, const uint8_t* __restrict__ scales_e,
-                                       int64_t n0, int64_t ndim, int64_t k0, int64_t kdim) {
-    const int row = threadIdx.x / kTPR, part = threadIdx.x % kTPR;
-    const int64_t n = n0 + row;
-#pragma unroll
-    for (int v = 0; v < kVec; ++v) {
-      const int64_t kb = k0 + (part * kVec + v) * 32;     // first k of this 32-block
-      if (n < ndim && kb < kdim) {
-        p[v] = *reinterpret_cast<const u32x4_t*>(packed_e + n * (kdim / 2) + kb / 2);
-        sb[v] = scales_e[n * (kdim / 32) + kb / 32];
-      } else {
-        p[v] = u32x4_t{0u, 0u, 0u, 0u};
-        sb[v] = 127u;
-      }
-    }
-  }
-  __device__ __forceinline__ void store(uint8_t* lds) const {
-    const int row = threadIdx.x / kTPR, part = threadIdx.x % kTPR;
-#pragma unroll
-    for (int v = 0; v < kVec; ++v) {
-      const float s = e8m0_to_f32(sb[v]);
-      uint8_t* dst = lds + row * kLdsRow + (part * kVec + v) * 64;
-      const uint32_t w[4] = {p[v].x, p[v].y, p[v].z, p[v].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {   // 8 codes -> 8 bf16 = 16 bytes
-        u32x4_t o = {dec_fp4_bf16x2<0>(w[q], s), dec_fp4_bf16x2<1>(w[q], s), dec_fp4_bf16x2<2>(w[q], s),
-                     dec_fp4_bf16x2<3>(w[q], s)};
-        *reinterpret_cast<u32x4_t*>(dst + q * 16) = o;
-      }
-    }
-  }
-};
-
-// ------------------------------------------------------ B operand, backward
-// Weight tile for grad_x = g W: 64 reduction rows (n) x BN output columns (k),
-// stored transposed in LDS as BN rows of 64 n-values.  Work item = 8 n x 8 k.
-template <int BN>
-struct BBwdLoader {
-  static constexpr int kItems = 8 * (BN / 8);    // (64/8) x (BN/8)
-  uint32_t p[8];   // 8 rows x 4 packed bytes (8 k values)
-  uint32_t sb[8];
-
-  __device__ __forceinline__ bool active() const { return (int)threadIdx.x < kItems; }
-
-  __device__ __forceinline__ void load(const uint8_t* __restrict__ packed_e, const uint8_t* __restrict__ scales_e,
-                                       int64_t n0, int64_t ndim, int64_t k0, int64_t kdim) {
-    if (!active()) return;
-    const int rg = threadIdx.x & 7, cg = threadIdx.x >> 3;
-    const int64_t k = k0 + cg * 8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t n = n0 + rg * 8 + i;
-      if (n < ndim && k < kdim) {
-        p[i] = *reinterpret_cast<const uint32_t*>(packed_e + n * (kdim / 2) + k / 2);
-        sb[i] = scales_e[n * (kdim / 32) + k / 32];
-      } else {
-        p[i] = 0u;
-        sb[i] = 127u;
-      }
-    }
-  }
-  __device__ __forceinline__ void store(uint8_t* lds) const {
-    if (!active()) return;
-    const int rg = threadIdx.x & 7, cg = threadIdx.x >> 3;
-    uint32_t d[8][4];   // d[row i][pair q] = bf16 of k = 2q (lo), 2q+1 (hi)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float s = e8m0_to_f32(sb[i]);
-      d[i][0] = dec_fp4_bf16x2<0>(p[i], s);
-      d[i][1] = dec_fp4_bf16x2<1>(p[i], s);
-      d[i][2] = dec_fp4_bf16x2<2>(p[i], s);
-      d[i][3] = dec_fp4_bf16x2<3>(p[i], s);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {   // output row = k column j of this block
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      u32x4_t o;
-      o.x = __builtin_amdgcn_perm(d[1][j >> 1], d[0][j >> 1], sel);
-      o.y = __builtin_amdgcn_perm(d[3][j >> 1], d[2][j >> 1], sel);
-      o.z = __builtin_amdgcn_perm(d[5][j >> 1], d[4][j >> 1], sel);
-      o.w = __builtin_amdgcn_perm(d[7][j >> 1], d[6][j >> 1], sel);
-      *reinterpret_cast<u32x4_t*>(lds + (cg * 8 + j) * kLdsRow + rg * 16) = o;
-    }
-  }
-};
-
-// ------------------------------------------------------------------ kernel
-template <int BM, int BN, bool BWD>
-__global__ void __launch_bounds__(kGemmThreads, 1)
-k_grouped_mm(const uint8_t* __restrict__ a,        // x [T, red] (fwd) or grad_out [T, red] (bwd), bf16
-             const uint8_t* __restrict__ packed,    // [E, N, K/2]
-             const uint8_t* __restrict__ scales,    // [E, N, K/32]
-             const int32_t* __restrict__ offs, int experts, int64_t tokens,
-             int64_t wn_dim, int64_t wk_dim,        // weight dims N, K
-             uint8_t* __restrict__ out) {           // [T, cols] bf16
-  constexpr int WM = BM / 2, WN = BN / 2, MT = WM / 32, NT = WN / 32;
-  // fwd: reduce over K, output columns N.  bwd: reduce over N, output columns K.
-  const int64_t red = BWD ? wn_dim : wk_dim;
-  const int64_t cols = BWD ? wk_dim : wn_dim;
-  const int64_t col0 = (int64_t)blockIdx.x * BN;
-
-  const TileInfo ti = find_tile<BM>(offs, experts, tokens, blockIdx.y);
-  if (ti.expert == -2) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  if (ti.expert == -1) {   // rows no expert owns: zeros
-    for (int i = threadIdx.x; i < BM * BN / 8; i += kGemmThreads) {
-      const int r = i / (BN / 8), c = (i % (BN / 8)) * 8;
-      const int64_t gr = ti.row0 + r, gc = col0 + c;
-      if (gr < ti.row_end && gc < cols) {
-        unsigned short* dst = reinterpret_cast<unsigned short*>(out + (gr * cols + gc) * 2);
-        for (int q = 0; q < 8 && gc + q < cols; ++q) dst[q] = 0;
-      }
-    }
-    return;
-  }
-
-  __shared__ GemmLds<BM, BN> lds;
-  const uint8_t* packed_e = packed + (int64_t)ti.expert * wn_dim * (wk_dim / 2);
-  const uint8_t* scales_e = scales + (int64_t)ti.expert * wn_dim * (wk_dim / 32);
-
-  ALoader<BM> al;
-  typename std::conditional<BWD, BBwdLoader<BN>, BFwdLoader<BN>>::type bl;
-
-  f32x16_t acc[MT][NT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[i][j] = f32x16_t{};
-
-  const int nsteps = (int)((red + kBK - 1) / kBK);
-  // weight tile origin: fwd (n = col0, k = step); bwd (n = step, k = col0)
-  auto load_step = [&](int s) {
-    const int64_t r0 = (int64_t)s * kBK;
-    al.load(a, red, ti.row0, ti.row_end, r0, red);
-    if constexpr (BWD) bl.load(packed_e, scales_e, r0, wn_dim, col0, wk_dim);
-    else bl.load(packed_e, scales_e, col0, wn_dim, r0, wk_dim);
-  };
-
-  load_step(0);
-  al.store(lds.a[0]);
-  bl.store(lds.b[0]);
-  __syncthreads();
-
-  const int frag_row = lane & 31, frag_k = (lane >> 5) * 16;   // byte offset of this lane's 8 k-values
-  for (int s = 0; s < nsteps; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nsteps) load_step(s + 1);
-    const uint8_t* la = lds.a[cur] + (wm * WM + frag_row) * kLdsRow + frag_k;
-    const uint8_t* lb = lds.b[cur] + (wn * WN + frag_row) * kLdsRow + frag_k;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8_t fa[MT], fb[NT];
-#pragma unroll
-      for (int i = 0; i < MT; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(la + i * 32 * kLdsRow + kk * 32);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) fb[j] = *reinterpret_cast<const bf16x8_t*>(lb + j * 32 * kLdsRow + kk * 32);
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    if (s + 1 < nsteps) {
-      al.store(lds.a[cur ^ 1]);
-      bl.store(lds.b[cur ^ 1]);
-    }
-    __syncthreads();
-  }
-
-  // epilogue: C[row][col], row = 8*(r/4) + 4*(lane/32) + r%4, col = lane%32
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int64_t gc = col0 + wn * WN + j * 32 + (lane & 31);
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const int64_t gr0 = ti.row0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        f32x2_t v = {acc[i][j][r], acc[i][j][r + 1]};
-        const uint32_t bb = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-        if (gc < cols) {
-          if (gr0 < ti.row_end) *reinterpret_cast<unsigned short*>(out + (gr0 * cols + gc) * 2) = (unsigned short)(bb & 0xFFFFu);
-          if (gr0 + 1 < ti.row_end) *reinterpret_cast<unsigned short*>(out + ((gr0 + 1) * cols + gc) * 2) = (unsigned short)(bb >> 16);
-        }
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------- forward, v2
-// Forward with the weight operand kept out of LDS.  The workgroup owns a
+// ------------------------------------------------- forward, general shapes
+// Forward with the weight operand kept out of LDS (any K % 32 == 0).  The workgroup owns a
 // 128 x 256 output tile; its 4 waves split the columns (wave tile 128 x 64,
 // 4 x 2 MFMA tiles).  Within a reduction step of 64, lane-half h takes the
 // 32 consecutive k [k0 + 32h, k0 + 32h + 32) -- one E8M0 scale block -- and
@@ -319,7 +114,7 @@ k_grouped_mm(const uint8_t* __restrict__ a,        // x [T, red] (fwd) or grad_o
 constexpr int kFwdBM = 128, kFwdBN = 256;
 
 __global__ void __launch_bounds__(kGemmThreads, 2)
-k_grouped_mm_fwd(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
+k_grouped_mm_fwd_general(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
                  const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
                  int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out) {
   constexpr int BM = kFwdBM, BN = kFwdBN, MT = BM / 32, NT = BN / 4 / 32;
@@ -436,8 +231,8 @@ k_grouped_mm_fwd(const uint8_t* __restrict__ a, const uint8_t* __restrict__ pack
   }
 }
 
-// ---------------------------------------------------------- forward, v3
-// Same tile and fragment scheme as v2, but every global transfer of the main
+// ------------------------------------------------------ forward, K % 128 == 0
+// Same tile and fragment scheme as the general forward, but every global transfer of the main
 // loop is a direct global->LDS DMA (global_load_lds_*), issued two steps
 // ahead into a ring of three LDS stages:
 //  * activations: the 128 x 64 bf16 tile (16 KB) as 16 blocks of 1 KB; a
@@ -485,7 +280,7 @@ struct V3Stage {
 };
 
 __global__ void __launch_bounds__(kGemmThreads, 2)
-k_grouped_mm_fwd_v3(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
+k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
                     const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
                     int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out) {
   constexpr int BM = kFwdBM, BN = kFwdBN, MT = BM / 32, NT = BN / 4 / 32;
@@ -621,13 +416,13 @@ k_grouped_mm_fwd_v3(const uint8_t* __restrict__ a, const uint8_t* __restrict__ p
   }
 }
 
-// ----------------------------------------------------------- backward, v2
+// ----------------------------------------------------------------- backward
 // grad_x = grad_out @ W_e.  Tile: 128 token rows x 256 output columns (k),
 // reduction over n in steps of 64; 4 waves split the columns (wave tile
 // 128 x 64), two workgroups per CU.
 //  * grad_out tile (128 x 64 bf16) is staged through registers into a
 //    double-buffered LDS tile (same (row >> 1) & 7 chunk swizzle as the
-//    forward), loaded one step ahead;
+//    DMA forward), loaded one step ahead;
 //  * weights: each wave builds a private transposed tile Wt[k][n] of its
 //    64 columns x 64 n in LDS.  Lane (nb, kb) = (lane % 8, lane / 8) owns the
 //    8 x 8 block n = 8nb.., k = 64*wave + 8kb..: it loads 8 packed dwords and
@@ -639,7 +434,7 @@ k_grouped_mm_fwd_v3(const uint8_t* __restrict__ a, const uint8_t* __restrict__ p
 constexpr int kBwdBM = 128, kBwdBN = 256;
 
 __global__ void __launch_bounds__(kGemmThreads, 2)
-k_grouped_mm_bwd_v2(const uint8_t* __restrict__ g, const uint8_t* __restrict__ packed,
+k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ packed,
                     const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
                     int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out) {
   constexpr int BM = kBwdBM, BN = kBwdBN, MT = BM / 32, NT = BN / 4 / 32;
@@ -795,19 +590,6 @@ k_grouped_mm_bwd_v2(const uint8_t* __restrict__ g, const uint8_t* __restrict__ p
 }
 
 // ------------------------------------------------------------------ launcher
-template <int BM, int BN, bool BWD>
-static hipError_t launch_t(const void* a, int64_t tokens, const int8_t* packed, const uint8_t* scales,
-                           int64_t experts, int64_t wn_dim, int64_t wk_dim, const int32_t* offs, void* out,
-                           hipStream_t st) {
-  const int64_t cols = BWD ? wk_dim : wn_dim;
-  const int64_t gx = (cols + BN - 1) / BN;
-  const int64_t gy = (tokens + BM - 1) / BM + experts;
-  hipLaunchKernelGGL((k_grouped_mm<BM, BN, BWD>), dim3((unsigned)gx, (unsigned)gy), dim3(kGemmThreads), 0, st,
-                     (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim,
-                     (uint8_t*)out);
-  return hipGetLastError();
-}
-
 hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8_t* packed, const uint8_t* scales,
                              int64_t experts, int64_t wn_dim, int64_t wk_dim, const int32_t* offs, void* out,
                              hipStream_t st) {
@@ -815,12 +597,12 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
     const int64_t gx = (wn_dim + kFwdBN - 1) / kFwdBN;
     const int64_t gy = (tokens + kFwdBM - 1) / kFwdBM + experts;
     if (wk_dim % 128 == 0 && ((uintptr_t)scales & 3) == 0) {
-      hipLaunchKernelGGL(k_grouped_mm_fwd_v3, dim3((unsigned)gx, (unsigned)gy), dim3(kGemmThreads), 0, st,
+      hipLaunchKernelGGL(k_grouped_mm_fwd_dma, dim3((unsigned)gx, (unsigned)gy), dim3(kGemmThreads), 0, st,
                          (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim,
                          wk_dim, (uint8_t*)out);
       return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_grouped_mm_fwd, dim3((unsigned)gx, (unsigned)gy), dim3(kGemmThreads), 0, st,
+    hipLaunchKernelGGL(k_grouped_mm_fwd_general, dim3((unsigned)gx, (unsigned)gy), dim3(kGemmThreads), 0, st,
                        (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim,
                        (uint8_t*)out);
     return hipGetLastError();
@@ -828,17 +610,11 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
   {
     const int64_t gx = (wk_dim + kBwdBN - 1) / kBwdBN;
     const int64_t gy = (tokens + kBwdBM - 1) / kBwdBM + experts;
-    hipLaunchKernelGGL(k_grouped_mm_bwd_v2, dim3((unsigned)gx, (unsigned)gy), dim3(kGemmThreads), 0, st,
+    hipLaunchKernelGGL(k_grouped_mm_bwd, dim3((unsigned)gx, (unsigned)gy), dim3(kGemmThreads), 0, st,
                        (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim,
                        (uint8_t*)out);
     return hipGetLastError();
   }
-  // Column tile: 256 when the output is wide, 128 otherwise (more tiles for small problems).
-  const int64_t cols = wk_dim;
-  const int64_t tiles256 = ((tokens + 255) / 256 + experts) * ((cols + 255) / 256);
-  if (tiles256 >= 1024)
-    return launch_t<256, 256, true>(a, tokens, packed, scales, experts, wn_dim, wk_dim, offs, out, st);
-  return launch_t<256, 128, true>(a, tokens, packed, scales, experts, wn_dim, wk_dim, offs, out, st);
 }
 
 }  // namespace mxq
