@@ -75,7 +75,7 @@ def main():
     dev = torch.device("cuda:0")
     L = mxq.lib()
     stream = torch.cuda.current_stream(dev)
-    sp = stream.cuda_stream
+    sp = stream.cuda_stream       # every leg runs on this stream; its events are recorded on it
     want = None if args.legs == "all" else [p.strip() for p in args.legs.split(",")]
 
     def wanted(name):   # a leg (or a group prefix of legs) asked for by --legs

@@ -5,8 +5,9 @@
 // load for 16-bit types, two for fp32); a scale block of B elements is B/8
 // consecutive lanes, whose amax is combined with DPP.  Every lane of a wave
 // runs the same trip count (tails are masked, never branched around) so the
-// cross-lane reductions always see whole groups.  Each lane keeps UNROLL
-// chunks in flight.  The general path (misaligned pointers, block sizes that
+// cross-lane reductions always see whole groups.  Each lane keeps several
+// chunks in flight (8 for inputs larger than the Infinity Cache, read
+// non-temporally; 4 otherwise).  The general path (misaligned pointers, block sizes that
 // are not a power of two in [8, 512], partial final groups) is one thread per
 // block with scalar accesses; it shares the element arithmetic.
 #include "launch.hpp"
@@ -15,7 +16,29 @@
 namespace mxq {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kGridCap = 16384;   // workgroups of a grid-stride launch (64 per CU)
+
+// Access mode of a streaming launch, chosen on the host by input size (MI355X
+// measurements): inputs larger than the 256 MB Infinity Cache stream best with
+// non-temporal loads and 8 chunks in flight per lane; smaller ones with plain
+// loads and 4.
+#ifndef MXQ_SMALL_NT_STORE
+#define MXQ_SMALL_NT_STORE 1
+#endif
+struct StreamBig {
+  static constexpr int kUnroll = 8;
+  template <typename T> __device__ static __forceinline__ T ld(const T* p) { return __builtin_nontemporal_load(p); }
+  template <typename T> __device__ static __forceinline__ void st(T v, T* p) { __builtin_nontemporal_store(v, p); }
+};
+struct StreamSmall {
+  static constexpr int kUnroll = 4;
+  template <typename T> __device__ static __forceinline__ T ld(const T* p) { return *p; }
+  template <typename T> __device__ static __forceinline__ void st(T v, T* p) {
+    if constexpr (MXQ_SMALL_NT_STORE) __builtin_nontemporal_store(v, p);
+    else *p = v;
+  }
+};
+constexpr int64_t kBigStreamBytes = 256ll << 20;
 
 template <int DT>
 struct Chunk {
@@ -23,29 +46,29 @@ struct Chunk {
   uint32_t w[kWords];
 };
 
-template <int DT>
+template <int DT, class M>
 __device__ __forceinline__ void load_chunk(const uint8_t* __restrict__ base, int64_t c, Chunk<DT>& ch) {
   if constexpr (DT == DT_F32) {
     const u32x4_t* p = reinterpret_cast<const u32x4_t*>(base + c * 32);
-    u32x4_t a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+    u32x4_t a = M::ld(p), b = M::ld(p + 1);
     ch.w[0] = a.x; ch.w[1] = a.y; ch.w[2] = a.z; ch.w[3] = a.w;
     ch.w[4] = b.x; ch.w[5] = b.y; ch.w[6] = b.z; ch.w[7] = b.w;
   } else {
-    u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(base + c * 16));
+    u32x4_t a = M::ld(reinterpret_cast<const u32x4_t*>(base + c * 16));
     ch.w[0] = a.x; ch.w[1] = a.y; ch.w[2] = a.z; ch.w[3] = a.w;
   }
 }
 
-template <int DT>
+template <int DT, class M>
 __device__ __forceinline__ void store_chunk(uint8_t* __restrict__ base, int64_t c, const Chunk<DT>& ch) {
   if constexpr (DT == DT_F32) {
     u32x4_t* p = reinterpret_cast<u32x4_t*>(base + c * 32);
     u32x4_t a = {ch.w[0], ch.w[1], ch.w[2], ch.w[3]}, b = {ch.w[4], ch.w[5], ch.w[6], ch.w[7]};
-    __builtin_nontemporal_store(a, p);
-    __builtin_nontemporal_store(b, p + 1);
+    M::st(a, p);
+    M::st(b, p + 1);
   } else {
     u32x4_t a = {ch.w[0], ch.w[1], ch.w[2], ch.w[3]};
-    __builtin_nontemporal_store(a, reinterpret_cast<u32x4_t*>(base + c * 16));
+    M::st(a, reinterpret_cast<u32x4_t*>(base + c * 16));
   }
 }
 
@@ -156,30 +179,30 @@ __device__ __forceinline__ void fake_quant_fp8_chunk(const Chunk<DT>& in, float 
 }
 
 // ------------------------------------------------------------- quantize_mxfp4
-template <int DT>
+template <int DT, class M>
 __global__ void __launch_bounds__(kThreads) k_quantize_mxfp4(const uint8_t* __restrict__ x,
                                                            uint32_t* __restrict__ packed,
                                                            uint8_t* __restrict__ scales, int64_t nchunks) {
-  const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
-  for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll; base < nchunks; base += step) {
-    Chunk<DT> ch[kUnroll];
+  const int64_t step = (int64_t)gridDim.x * kThreads * M::kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * M::kUnroll; base < nchunks; base += step) {
+    Chunk<DT> ch[M::kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < M::kUnroll; ++u) {
       const int64_t c = base + u * kThreads + threadIdx.x;
-      if (c < nchunks) load_chunk<DT>(x, c, ch[u]);
+      if (c < nchunks) load_chunk<DT, M>(x, c, ch[u]);
       else {
 #pragma unroll
         for (int i = 0; i < Chunk<DT>::kWords; ++i) ch[u].w[i] = 0u;
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < M::kUnroll; ++u) {
       const int64_t c = base + u * kThreads + threadIdx.x;
       const uint32_t amax = group_max_u32<4>(chunk_amax_bits<DT>(ch[u]));   // 32 = 4 chunks
       const int e = floor_rule_exponent(amax);
       const uint32_t codes = encode_fp4_chunk<DT, true>(ch[u], pow2f(e));
       if (c < nchunks) {
-        __builtin_nontemporal_store(codes, packed + c);
+        M::st(codes, packed + c);
         if ((c & 3) == 0) scales[c >> 2] = (uint8_t)(e + 127);
       }
     }
@@ -221,25 +244,25 @@ __global__ void __launch_bounds__(kThreads) k_quantize_mxfp4_general(const uint8
 }
 
 // ----------------------------------------------------------- dequantize_mxfp4
-template <int DT>
+template <int DT, class M>
 __global__ void __launch_bounds__(kThreads) k_dequantize_mxfp4(const uint32_t* __restrict__ packed,
                                                              const uint8_t* __restrict__ scales,
                                                              uint8_t* __restrict__ out, int64_t nchunks) {
-  const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
-  for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll; base < nchunks; base += step) {
-    uint32_t codes[kUnroll], sb[kUnroll];
+  const int64_t step = (int64_t)gridDim.x * kThreads * M::kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * M::kUnroll; base < nchunks; base += step) {
+    uint32_t codes[M::kUnroll], sb[M::kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < M::kUnroll; ++u) {
       const int64_t c = base + u * kThreads + threadIdx.x;
-      codes[u] = c < nchunks ? __builtin_nontemporal_load(packed + c) : 0u;
+      codes[u] = c < nchunks ? M::ld(packed + c) : 0u;
       sb[u] = c < nchunks ? (uint32_t)scales[c >> 2] : 127u;
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < M::kUnroll; ++u) {
       const int64_t c = base + u * kThreads + threadIdx.x;
       Chunk<DT> o;
       decode_fp4_chunk<DT>(clear_negzero_codes(codes[u]), e8m0_to_f32(sb[u]), o);
-      if (c < nchunks) store_chunk<DT>(out, c, o);
+      if (c < nchunks) store_chunk<DT, M>(out, c, o);
     }
   }
 }
@@ -266,30 +289,30 @@ __global__ void __launch_bounds__(kThreads) k_dequantize_mxfp4_general(const uin
 }
 
 // ------------------------------------------------------------- quantize_cache
-template <int DT, int FMT, int L>
+template <int DT, int FMT, int L, class M>
 __global__ void __launch_bounds__(kThreads) k_quantize_cache(const uint8_t* __restrict__ x,
                                                            uint8_t* __restrict__ out, int64_t nchunks) {
-  const int64_t step = (int64_t)gridDim.x * kThreads * kUnroll;
-  for (int64_t base = (int64_t)blockIdx.x * kThreads * kUnroll; base < nchunks; base += step) {
-    Chunk<DT> ch[kUnroll];
+  const int64_t step = (int64_t)gridDim.x * kThreads * M::kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * M::kUnroll; base < nchunks; base += step) {
+    Chunk<DT> ch[M::kUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < M::kUnroll; ++u) {
       const int64_t c = base + u * kThreads + threadIdx.x;
-      if (c < nchunks) load_chunk<DT>(x, c, ch[u]);
+      if (c < nchunks) load_chunk<DT, M>(x, c, ch[u]);
       else {
 #pragma unroll
         for (int i = 0; i < Chunk<DT>::kWords; ++i) ch[u].w[i] = 0u;
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < M::kUnroll; ++u) {
       const int64_t c = base + u * kThreads + threadIdx.x;
       const uint32_t amax = group_max_u32<L>(chunk_amax_bits<DT>(ch[u]));
       const float s = pow2f(ceil_rule_exponent<FMT>(amax));
       Chunk<DT> o;
       if constexpr (FMT == FMT_FP8) fake_quant_fp8_chunk<DT>(ch[u], s, o);
       else decode_fp4_chunk<DT>(clear_negzero_codes(encode_fp4_chunk<DT, false>(ch[u], s)), s, o);
-      if (c < nchunks) store_chunk<DT>(out, c, o);
+      if (c < nchunks) store_chunk<DT, M>(out, c, o);
     }
   }
 }
@@ -334,11 +357,23 @@ __global__ void __launch_bounds__(kThreads) k_quantize_cache_general(const uint8
 }
 
 // ------------------------------------------------------------ STE copy
+template <class M>
 __global__ void __launch_bounds__(kThreads) k_copy16(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
                                                    int64_t n16) {
-  const int64_t step = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += step)
-    __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+  const int64_t step = (int64_t)gridDim.x * kThreads * M::kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * M::kUnroll; base < n16; base += step) {
+    u32x4_t v[M::kUnroll];
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u) {
+      const int64_t i = base + u * kThreads + threadIdx.x;
+      if (i < n16) v[u] = M::ld(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u) {
+      const int64_t i = base + u * kThreads + threadIdx.x;
+      if (i < n16) M::st(v[u], dst + i);
+    }
+  }
 }
 __global__ void __launch_bounds__(kThreads) k_copy_bytes(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                                        int64_t n) {
@@ -354,7 +389,7 @@ __global__ void __launch_bounds__(kThreads) k_zero_bytes(uint8_t* __restrict__ d
 // ------------------------------------------------------------------ launchers
 static inline int grid_for(int64_t items, int64_t per_block) {
   int64_t g = (items + per_block - 1) / per_block;
-  const int64_t cap = 256 * 16;   // 256 CUs x 16 blocks of 4 waves: enough to fill the chip
+  const int64_t cap = kGridCap;
   return (int)(g < 1 ? 1 : (g > cap ? cap : g));
 }
 static inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -365,8 +400,12 @@ static hipError_t launch_quantize_mxfp4_t(const void* x, int64_t rows, int64_t k
   const int64_t n = rows * k;
   if (aligned(x, 16) && aligned(packed, 4)) {
     const int64_t nchunks = n / 8;
-    hipLaunchKernelGGL(k_quantize_mxfp4<DT>, dim3(grid_for(nchunks, kThreads * kUnroll)), dim3(kThreads), 0, st,
-                       (const uint8_t*)x, (uint32_t*)packed, scales, nchunks);
+    if (n * (DT == DT_F32 ? 4 : 2) >= kBigStreamBytes)
+      hipLaunchKernelGGL((k_quantize_mxfp4<DT, StreamBig>), dim3(grid_for(nchunks, kThreads * StreamBig::kUnroll)),
+                         dim3(kThreads), 0, st, (const uint8_t*)x, (uint32_t*)packed, scales, nchunks);
+    else
+      hipLaunchKernelGGL((k_quantize_mxfp4<DT, StreamSmall>), dim3(grid_for(nchunks, kThreads * StreamSmall::kUnroll)),
+                         dim3(kThreads), 0, st, (const uint8_t*)x, (uint32_t*)packed, scales, nchunks);
   } else {
     const int64_t nb = n / 32;
     hipLaunchKernelGGL(k_quantize_mxfp4_general<DT>, dim3(grid_for(nb, kThreads)), dim3(kThreads), 0, st,
@@ -389,9 +428,11 @@ static hipError_t launch_dequantize_mxfp4_t(const int8_t* packed, const uint8_t*
                                             void* out, hipStream_t st) {
   const int64_t n = rows * k;
   if (aligned(packed, 4) && aligned(out, 16)) {
+    // dequantization is write-dominated (1 packed byte -> 4..8 output bytes):
+    // plain loads measured best at every size
     const int64_t nchunks = n / 8;
-    hipLaunchKernelGGL(k_dequantize_mxfp4<DT>, dim3(grid_for(nchunks, kThreads * kUnroll)), dim3(kThreads), 0, st,
-                       (const uint32_t*)packed, scales, (uint8_t*)out, nchunks);
+    hipLaunchKernelGGL((k_dequantize_mxfp4<DT, StreamSmall>), dim3(grid_for(nchunks, kThreads * StreamSmall::kUnroll)),
+                       dim3(kThreads), 0, st, (const uint32_t*)packed, scales, (uint8_t*)out, nchunks);
   } else {
     const int64_t nb = n / 32;
     hipLaunchKernelGGL(k_dequantize_mxfp4_general<DT>, dim3(grid_for(nb, kThreads)), dim3(kThreads), 0, st,
@@ -411,8 +452,13 @@ hipError_t launch_dequantize_mxfp4(const int8_t* packed, const uint8_t* scales, 
 
 template <int DT, int FMT, int L>
 static void launch_cache_fast(const void* x, void* out, int64_t nchunks, hipStream_t st) {
-  hipLaunchKernelGGL((k_quantize_cache<DT, FMT, L>), dim3(grid_for(nchunks, kThreads * kUnroll)), dim3(kThreads), 0,
-                     st, (const uint8_t*)x, (uint8_t*)out, nchunks);
+  if (nchunks * 8 * (DT == DT_F32 ? 4 : 2) >= kBigStreamBytes)
+    hipLaunchKernelGGL((k_quantize_cache<DT, FMT, L, StreamBig>), dim3(grid_for(nchunks, kThreads * StreamBig::kUnroll)),
+                       dim3(kThreads), 0, st, (const uint8_t*)x, (uint8_t*)out, nchunks);
+  else
+    hipLaunchKernelGGL((k_quantize_cache<DT, FMT, L, StreamSmall>),
+                       dim3(grid_for(nchunks, kThreads * StreamSmall::kUnroll)), dim3(kThreads), 0, st,
+                       (const uint8_t*)x, (uint8_t*)out, nchunks);
 }
 
 template <int DT, int FMT>
@@ -460,8 +506,12 @@ hipError_t launch_quantize_cache(const void* x, void* out, int dt, int64_t rows,
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st) {
   if (aligned(src, 16) && aligned(dst, 16) && bytes % 16 == 0) {
     const int64_t n16 = bytes / 16;
-    hipLaunchKernelGGL(k_copy16, dim3(grid_for(n16, kThreads * 4)), dim3(kThreads), 0, st, (const u32x4_t*)src,
-                       (u32x4_t*)dst, n16);
+    if (bytes >= kBigStreamBytes)
+      hipLaunchKernelGGL(k_copy16<StreamBig>, dim3(grid_for(n16, kThreads * StreamBig::kUnroll)), dim3(kThreads), 0,
+                         st, (const u32x4_t*)src, (u32x4_t*)dst, n16);
+    else
+      hipLaunchKernelGGL(k_copy16<StreamSmall>, dim3(grid_for(n16, kThreads * StreamSmall::kUnroll)), dim3(kThreads),
+                         0, st, (const u32x4_t*)src, (u32x4_t*)dst, n16);
   } else {
     hipLaunchKernelGGL(k_copy_bytes, dim3(grid_for(bytes, kThreads * 4)), dim3(kThreads), 0, st,
                        (const uint8_t*)src, (uint8_t*)dst, bytes);

@@ -519,12 +519,18 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
         d[i][3] = dec_fp4_bf16x2<3>(p, sc);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {   // Wt row k = 8kb + j, logical chunk nb, 8-byte half `half`
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+      for (int j = 0; j < 8; ++j) {
+        // Wt row k = 8kb + jj, logical chunk nb, 8-byte half `half`.  Lanes with
+        // odd kb write the rows of each pair in swapped order (jj = j ^ 1), so
+        // one instruction writes rows of both parities, i.e. both 128-byte
+        // halves of the 256-byte bank space (LDS takes 32 lanes x 8 bytes per
+        // cycle), instead of piling into one.
+        const int jj = j ^ (kb & 1);
+        const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
         u32x2_t o;
         o.x = __builtin_amdgcn_perm(d[1][j >> 1], d[0][j >> 1], sel);
         o.y = __builtin_amdgcn_perm(d[3][j >> 1], d[2][j >> 1], sel);
-        const int k = kb * 8 + j;
+        const int k = kb * 8 + jj;
         *reinterpret_cast<u32x2_t*>(wt + k * 128 + 16 * (nb ^ ((k >> 1) & 7)) + 8 * half) = o;
       }
     }
