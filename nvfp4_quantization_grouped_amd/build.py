@@ -7,6 +7,7 @@ nvfp4_quantization_grouped_amd/libmxq.so.  hipcc cross-compiles, so this runs
 on a machine without a GPU.
 """
 
+import ctypes
 import os
 import shutil
 import subprocess
@@ -61,6 +62,12 @@ def build(verbose=True, extra_flags=()):
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # an unresolved kernel stub only shows up at load time: load it here
+    try:
+        ctypes.CDLL(tmp)
+    except OSError as e:
+        os.remove(tmp)
+        raise RuntimeError(f"built library does not load: {e}") from None
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
