@@ -8,10 +8,12 @@
 // The bf16 weight never exists in HBM.  fp32 accumulation, bf16
 // nearest-even output.
 //
-// All kernels: 256 threads (4 waves) own a 128-row x 256-column output tile;
-// the waves split the columns (wave tile 128 x 64 = 4 x 2 MFMA tiles, 128
-// fp32 accumulators per lane), and two workgroups share a CU so one's
-// memory phase overlaps the other's MFMAs.  The reduction runs in steps of
+// Every wave owns a 128-row x 64-column output tile (4 x 2 MFMA tiles, 128
+// fp32 accumulators per lane) and runs two to a SIMD, so one's memory phase
+// overlaps the other's MFMAs.  Workgroups of 4 waves (128 x 256 tiles, two
+// per CU) serve every shape; large forwards use workgroups of 8 waves
+// (128 x 512 tiles, one per CU), which move half the activation bytes per
+// output element.  The reduction runs in steps of
 // 64, and inside a step lane-half h of a wave covers the 32 consecutive
 // reduction indices [32h, 32h + 32) -- for the forward exactly one E8M0
 // scale block -- with sub-step kk taking the 8 values 32h + 8kk ..; both
@@ -232,8 +234,9 @@ k_grouped_mm_fwd_general(const uint8_t* __restrict__ a, const uint8_t* __restric
 }
 
 // ------------------------------------------------------ forward, K % 128 == 0
-// Same tile and fragment scheme as the general forward, but every global transfer of the main
-// loop is a direct global->LDS DMA (global_load_lds_*), issued two steps
+// Same wave tile and fragment scheme as the general forward, with W = 4 or
+// 8 waves side by side along the columns, and every global transfer of the
+// main loop a direct global->LDS DMA (global_load_lds_*), issued two steps
 // ahead into a ring of three LDS stages:
 //  * activations: the 128 x 64 bf16 tile (16 KB) as 16 blocks of 1 KB; a
 //    block holds 8 rows, and within a row the eight 16-byte chunks are
@@ -244,8 +247,12 @@ k_grouped_mm_fwd_general(const uint8_t* __restrict__ a, const uint8_t* __restric
 //  * weights: each wave fetches the packed bytes of its own 64 weight rows
 //    (2 blocks of 1 KB, laid out [row/32][half][row%32] x 16 bytes, so a
 //    lane's 16 bytes -- one 32-k scale block -- sit next to its neighbours')
-//    and their scale bytes (the aligned dword holding this step's two
-//    32-k blocks and the neighbouring step's, 4 bytes per lane);
+//    and their scale bytes, either the aligned dword holding this step's
+//    two 32-k blocks and the neighbouring step's (4 bytes per lane, every
+//    step) or, when K % 512 == 0, 16 bytes covering 8 steps, every 8 steps.
+//    The per-lane cost of these transfers follows the cache lines they
+//    touch (a weight block touches 32 lines for 1 KB, a scale dword
+//    transfer 64 lines for 256 bytes), so the 8-step scale chunks matter;
 //  * each step waits for exactly the DMA of the step it is about to use
 //    (s_waitcnt vmcnt(N), N = operations issued after it), then barriers.
 // With no register-destined loads in the loop, no other waits are needed.
@@ -254,12 +261,6 @@ k_grouped_mm_fwd_general(const uint8_t* __restrict__ a, const uint8_t* __restric
 // in-bounds and land in a stage nobody reads.  Rows past the expert's segment
 // load a clamped valid row and are never stored; weight rows past N
 // likewise.  Needs K % 128 == 0 (4-byte aligned scale rows).
-constexpr int kV3Stages = 3;
-constexpr int kV3ABytes = kFwdBM * 128;          // 16 KB, unpadded (swizzled)
-constexpr int kV3BBytes = kFwdBN * 32;           // 8 KB packed weights
-constexpr int kV3SBytes = kFwdBN * 4;            // 1 KB scales (4 bytes = 2 steps per row)
-constexpr int kV3DmaPerStep = 4 + 2 + 1;         // per wave: A, packed B, scales
-
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -273,17 +274,81 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-struct V3Stage {
-  uint8_t a[kV3ABytes];
-  uint8_t b[kV3BBytes];
-  uint8_t s[kV3SBytes];
+constexpr int kDmaABytes = kFwdBM * 128;          // 16 KB activation tile per step, unpadded (swizzled)
+
+// LDS of the DMA forward for a workgroup of W waves (W x 64 output columns).
+// A stage holds one step's activation tile and packed weight bytes (32 per
+// column).  Scales come in chunks of SCH steps: SCH = 2 puts each column's
+// dword (2 steps x 2 blocks) in every stage; SCH = 8 keeps a separate
+// double buffer of 16 bytes (8 steps) per column, refilled every 8 steps,
+// so the scale transfer touches each column's cache line once per 8 steps
+// instead of once per step.
+template <int W, int SCH>
+struct DmaStage {                                           // SCH == 8: no scales per stage
+  uint8_t a[kDmaABytes];
+  uint8_t b[W * 64 * 32];
+};
+template <int W>
+struct DmaStage<W, 2> {
+  uint8_t a[kDmaABytes];
+  uint8_t b[W * 64 * 32];
+  uint8_t s[W * 64 * 4];
+};
+template <int W, int STAGES, int SCH>
+struct DmaSmem {
+  static constexpr int kCols = W * 64;
+  static constexpr int kABlocksPerWave = 16 / W;            // 1 KB activation blocks each wave moves
+  using Stage = DmaStage<W, SCH>;
+  Stage st[STAGES];
+  uint8_t s8[2][kCols * 16];
+};
+template <int W, int STAGES>
+struct DmaSmem<W, STAGES, 2> {
+  static constexpr int kCols = W * 64;
+  static constexpr int kABlocksPerWave = 16 / W;
+  using Stage = DmaStage<W, 2>;
+  Stage st[STAGES];
 };
 
-__global__ void __launch_bounds__(kGemmThreads, 2)
+// One step's activation and weight transfers of one wave, straight into LDS
+// (plus the per-step scale dword when SCH == 2).
+template <int W, int STAGES, int SCH>
+__device__ __forceinline__ void fwd_dma_issue(typename DmaSmem<W, STAGES, SCH>::Stage& d,
+                                              const uint8_t* const (&a_src)[16 / W],
+                                              const uint8_t* const (&b_src)[2], const uint8_t* s_src, int wave,
+                                              int step) {
+  constexpr int QA = DmaSmem<W, STAGES, SCH>::kABlocksPerWave;
+  const int64_t ka = (int64_t)step * kBK * 2;     // activation bytes
+  const int64_t kb = (int64_t)step * 32;          // packed bytes
+#pragma unroll
+  for (int q = 0; q < QA; ++q)
+    __builtin_amdgcn_global_load_lds(a_src[q] + ka, (lds_void_t*)(d.a + 1024 * (QA * wave + q)), 16, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    __builtin_amdgcn_global_load_lds(b_src[j] + kb, (lds_void_t*)(d.b + 2048 * wave + 1024 * j), 16, 0, 0);
+  if constexpr (SCH == 2)
+    __builtin_amdgcn_global_load_lds(s_src + 4 * (step >> 1), (lds_void_t*)(d.s + 256 * wave), 4, 0, 0);
+}
+
+// The 16-byte scale chunk c (steps 8c .. 8c+7) of this wave's 64 columns.
+template <int W, int STAGES>
+__device__ __forceinline__ void fwd_dma_scales8(DmaSmem<W, STAGES, 8>& sm, const uint8_t* s_src, int wave, int chunk) {
+  __builtin_amdgcn_global_load_lds(s_src + 16 * chunk, (lds_void_t*)(sm.s8[chunk & 1] + 1024 * wave), 16, 0, 0);
+}
+
+template <int W, int STAGES, int MINWG, int SCH>
+__global__ void __launch_bounds__(W * 64, MINWG)
 k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
-                    const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
-                    int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out) {
-  constexpr int BM = kFwdBM, BN = kFwdBN, MT = BM / 32, NT = BN / 4 / 32;
+                     const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
+                     int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out) {
+  static_assert(SCH == 2 || SCH == 8, "scale chunk");
+  // with SCH == 8 the step-end wait below counts the scale transfer of this
+  // step only, which is exact for a ring of three stages
+  static_assert(SCH == 2 || STAGES == 3, "scale chunk accounting assumes 3 stages");
+  using Smem = DmaSmem<W, STAGES, SCH>;
+  constexpr int BM = kFwdBM, BN = Smem::kCols, MT = BM / 32, NT = 2, QA = Smem::kABlocksPerWave;
+  constexpr int kOps = QA + 2 + (SCH == 2 ? 1 : 0);   // per wave and step (plus 1 every 8 steps when SCH == 8)
+  constexpr int kThreads = W * 64;
   const int64_t col0 = (int64_t)blockIdx.x * BN;
   const TileInfo ti = find_tile<BM>(offs, experts, tokens, blockIdx.y);
   if (ti.expert == -2) return;
@@ -291,7 +356,7 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
   const int h = lane >> 5, r = lane & 31;
 
   if (ti.expert == -1) {
-    for (int i = threadIdx.x; i < BM * BN / 8; i += kGemmThreads) {
+    for (int i = threadIdx.x; i < BM * BN / 8; i += kThreads) {
       const int rr = i / (BN / 8), c = (i % (BN / 8)) * 8;
       const int64_t gr = ti.row0 + rr, gc = col0 + c;
       if (gr < ti.row_end && gc < ndim) {
@@ -302,47 +367,36 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
     return;
   }
 
-  __shared__ __attribute__((aligned(1024))) V3Stage st[kV3Stages];
+  __shared__ __attribute__((aligned(1024))) Smem sm;
 
-  // activation DMA: this wave fills A blocks 4*wave .. 4*wave+3; block b holds
-  // rows 8b .. 8b+7: lane l -> row 8b + l/8, LDS chunk l%8 <- global chunk
-  // (l%8) ^ ((row >> 1) & 7)
-  const uint8_t* a_src[4];
+  // activation DMA: this wave fills A blocks QA*wave .. QA*wave+QA-1; block b
+  // holds rows 8b .. 8b+7: lane l -> row 8b + l/8, LDS chunk l%8 <- global
+  // chunk (l%8) ^ ((row >> 1) & 7)
+  const uint8_t* a_src[QA];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = 8 * (4 * wave + q) + (lane >> 3);
+  for (int q = 0; q < QA; ++q) {
+    const int row = 8 * (QA * wave + q) + (lane >> 3);
     int64_t grow = ti.row0 + row;
     if (grow >= ti.row_end) grow = ti.row_end - 1;
     a_src[q] = a + (grow * kdim + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2;
   }
   // weight DMA: this wave's rows n = col0 + 64*wave + 32*j + r (j = 0, 1);
-  // block j holds [half h][row r] x 16 bytes; scales: 2 bytes per row
+  // block j holds [half h][row r] x 16 bytes.  Scales: lane l covers column
+  // 64*wave + l (a dword per step pair, or 16 bytes per 8 steps).
   const uint8_t* packed_e = packed_e_of(packed, ti.expert, ndim, kdim);
   const uint8_t* b_src[NT];
   bool wok[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    int64_t n = col0 + wave * (BN / 4) + j * 32 + r;
+    int64_t n = col0 + wave * 64 + j * 32 + r;
     wok[j] = n < ndim;
     if (!wok[j]) n = ndim - 1;
     b_src[j] = packed_e + n * (kdim / 2) + 16 * h;
   }
-  int64_t n_s = col0 + wave * (BN / 4) + lane;
+  int64_t n_s = col0 + wave * 64 + lane;
   if (n_s >= ndim) n_s = ndim - 1;
-  const uint8_t* s_src = scales + ((int64_t)ti.expert * ndim + n_s) * (kdim / 32);   // 4-byte aligned: K % 128 == 0
-
-  auto dma_step = [&](int step, int stage) {
-    V3Stage& d = st[stage];
-    const int64_t ka = (int64_t)step * kBK * 2;     // activation bytes
-    const int64_t kb = (int64_t)step * 32;          // packed bytes
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      __builtin_amdgcn_global_load_lds(a_src[q] + ka, (lds_void_t*)(d.a + 4096 * wave + 1024 * q), 16, 0, 0);
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-      __builtin_amdgcn_global_load_lds(b_src[j] + kb, (lds_void_t*)(d.b + 2048 * wave + 1024 * j), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(s_src + 4 * (step >> 1), (lds_void_t*)(d.s + 256 * wave), 4, 0, 0);
-  };
+  // 4-byte aligned rows for SCH == 2 (K % 128 == 0), 16-byte for SCH == 8 (K % 512 == 0)
+  const uint8_t* s_src = scales + ((int64_t)ti.expert * ndim + n_s) * (kdim / 32);
 
   f32x16_t acc[MT][NT];
 #pragma unroll
@@ -352,22 +406,40 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
 
   const int nsteps = (int)(kdim / kBK);
   const int last = nsteps - 1;
-  dma_step(0, 0);
-  dma_step(min(1, last), 1);
-  wait_vmcnt_barrier<kV3DmaPerStep>();          // step 0 landed; step 1 may be in flight
+  const int last_chunk = (nsteps - 1) >> 3;
+  if constexpr (SCH == 8) fwd_dma_scales8<W, STAGES>(sm, s_src, wave, 0);
+#pragma unroll
+  for (int t = 0; t < STAGES - 1; ++t)
+    fwd_dma_issue<W, STAGES, SCH>(sm.st[t], a_src, b_src, s_src, wave, min(t, last));
+  // step 0 (and scale chunk 0) have landed once only steps 1 .. STAGES-2 may be in flight
+  wait_vmcnt_barrier<kOps * (STAGES - 2)>();
 
   const int swz_base = r * 128;
   int stage = 0;
   for (int s = 0; s < nsteps; ++s) {
     __builtin_amdgcn_sched_barrier(0);
-    dma_step(min(s + 2, last), stage == 0 ? 2 : stage - 1);   // stage (s+2) % 3
-    const V3Stage& c = st[stage];
+    // scale chunk c+1 goes out at the first step of chunk c, ahead of this
+    // step's activation and weight transfers (vmcnt counts in issue order)
+    const bool chunk_start = SCH == 8 && (s & 7) == 0;
+    if constexpr (SCH == 8) {
+      if (chunk_start) fwd_dma_scales8<W, STAGES>(sm, s_src, wave, min((s >> 3) + 1, last_chunk));
+    }
+    // refill the stage step s-1 used with step s + STAGES - 1
+    fwd_dma_issue<W, STAGES, SCH>(sm.st[stage == 0 ? STAGES - 1 : stage - 1], a_src, b_src, s_src, wave,
+                                  min(s + STAGES - 1, last));
+    const typename Smem::Stage& c = sm.st[stage];
     // decode this wave's weights for the step into B fragments
     bf16x8_t fb[NT][4];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const u32x4_t p = *reinterpret_cast<const u32x4_t*>(c.b + 2048 * wave + 1024 * j + 512 * h + 16 * r);
-      const float sc = e8m0_to_f32(c.s[4 * (wave * 64 + j * 32 + r) + 2 * (s & 1) + h]);
+      const int col = wave * 64 + j * 32 + r;
+      uint8_t sb;
+      if constexpr (SCH == 2)
+        sb = c.s[4 * col + 2 * (s & 1) + h];
+      else
+        sb = sm.s8[(s >> 3) & 1][16 * col + 2 * (s & 7) + h];
+      const float sc = e8m0_to_f32(sb);
       const uint32_t w[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -389,10 +461,15 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
         for (int j = 0; j < NT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j][kk], acc[i][j], 0, 0, 0);
     }
-    // step s+1 has landed once only the DMA of step s+2 may be in flight
-    wait_vmcnt_barrier<kV3DmaPerStep>();
+    // step s+1 (and its scale chunk) have landed once only the transfers
+    // issued after step s+1's may be in flight: steps s+2 .. s+STAGES-1, and
+    // this step's scale chunk
+    if (chunk_start)
+      wait_vmcnt_barrier<kOps * (STAGES - 2) + 1>();
+    else
+      wait_vmcnt_barrier<kOps * (STAGES - 2)>();
     __builtin_amdgcn_sched_barrier(0);
-    stage = stage == kV3Stages - 1 ? 0 : stage + 1;
+    stage = stage == STAGES - 1 ? 0 : stage + 1;
   }
   // drain the clamped tail transfers before this workgroup's LDS is released
   __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
@@ -401,7 +478,7 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
   for (int i = 0; i < MT; ++i) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int64_t gc = col0 + wave * (BN / 4) + j * 32 + r;
+      const int64_t gc = col0 + wave * 64 + j * 32 + r;
 #pragma unroll
       for (int q = 0; q < 16; q += 2) {
         const int64_t gr0 = ti.row0 + i * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
@@ -603,9 +680,24 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
     const int64_t gx = (wn_dim + kFwdBN - 1) / kFwdBN;
     const int64_t gy = (tokens + kFwdBM - 1) / kFwdBM + experts;
     if (wk_dim % 128 == 0 && ((uintptr_t)scales & 3) == 0) {
-      hipLaunchKernelGGL(k_grouped_mm_fwd_dma, dim3((unsigned)gx, (unsigned)gy), dim3(kGemmThreads), 0, st,
-                         (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim,
-                         wk_dim, (uint8_t*)out);
+#ifndef MXQ_FWD_WIDE
+#define MXQ_FWD_WIDE 1
+#endif
+#ifndef MXQ_FWD_SCH8
+#define MXQ_FWD_SCH8 1
+#endif
+      const bool sch8 = MXQ_FWD_SCH8 && wk_dim % 512 == 0 && ((uintptr_t)scales & 15) == 0;
+      const int64_t gx8 = (wn_dim + 511) / 512;
+      const bool wide = MXQ_FWD_WIDE && gx8 * gy >= 2 * 256;
+      const dim3 g4((unsigned)gx, (unsigned)gy), g8((unsigned)gx8, (unsigned)gy);
+#define MXQ_FWD_LAUNCH(W, ST, WG, SCH, G)                                                                    \
+  hipLaunchKernelGGL((k_grouped_mm_fwd_dma<W, ST, WG, SCH>), G, dim3(W * 64), 0, st, (const uint8_t*)a,      \
+                     (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim, (uint8_t*)out)
+      if (wide && sch8) MXQ_FWD_LAUNCH(8, 3, 1, 8, g8);
+      else if (wide) MXQ_FWD_LAUNCH(8, 3, 1, 2, g8);
+      else if (sch8) MXQ_FWD_LAUNCH(4, 3, 2, 8, g4);
+      else MXQ_FWD_LAUNCH(4, 3, 2, 2, g4);
+#undef MXQ_FWD_LAUNCH
       return hipGetLastError();
     }
     hipLaunchKernelGGL(k_grouped_mm_fwd_general, dim3((unsigned)gx, (unsigned)gy), dim3(kGemmThreads), 0, st,

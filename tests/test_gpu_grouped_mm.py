@@ -82,8 +82,10 @@ def test_one_hot_weights_bit_exact():
     (8, 1500, 512, 1024, [300, 1, 255, 257, 0, 0, 400, 287]),
     (3, 600, 1024, 2048, [0, 600, 0]),
     (5, 2048, 2048, 512, [512, 512, 512, 256, 256]),
-    # many tiles and a column tail (1032 = 4 x 256 + 8)
+    # many tiles and a column tail (1032 = 4 x 256 + 8); K = 256 (per-step scale transfers)
     (4, 44000, 1032, 256, [11000, 0, 20999, 12001]),
+    # the same with K = 1024 (8-step scale chunks) and a 150-row uncovered tail
+    (4, 40000, 1032, 1024, [10000, 0, 19850, 10000]),
 ])
 def test_random_segments(E, T, N, K, counts):
     offs = np.cumsum(counts).astype(np.int32)
