@@ -496,24 +496,43 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
 // ----------------------------------------------------------------- backward
 // grad_x = grad_out @ W_e.  Tile: 128 token rows x 256 output columns (k),
 // reduction over n in steps of 64; 4 waves split the columns (wave tile
-// 128 x 64), two workgroups per CU.
+// 128 x 64), two workgroups per CU.  All global loads go to registers one
+// step ahead (addresses clamped into range, out-of-range values replaced by
+// zeros), so the compiler's in-order vmcnt accounting stays exact.
 //  * grad_out tile (128 x 64 bf16) is staged through registers into a
 //    double-buffered LDS tile (same (row >> 1) & 7 chunk swizzle as the
-//    DMA forward), loaded one step ahead;
-//  * weights: each wave builds a private transposed tile Wt[k][n] of its
-//    64 columns x 64 n in LDS.  Lane (nb, kb) = (lane % 8, lane / 8) owns the
-//    8 x 8 block n = 8nb.., k = 64*wave + 8kb..: it loads 8 packed dwords and
-//    the 8 rows' scale bytes one step ahead, decodes them (scaled fp4 ->
-//    bf16), regroups the 8 x 8 block with v_perm into 8 rows of 8 n-values and
-//    writes them to Wt, which only its own wave reads (no barrier needed);
+//    DMA forward);
+//  * weights: lane l of a wave fetches the 32 packed bytes (64 values) of
+//    weight row n0 + l in the wave's 64 columns and their two scale bytes,
+//    decodes them along k -- the direction the scaled fp4 conversion and
+//    the E8M0 block both run -- and writes the bf16 row, in 16-byte chunks,
+//    into a wave-private tile Wd[n][k] (no barrier needed);
+//  * the B fragments, which need 8 consecutive n of one column per lane,
+//    come out of Wd with gfx950's transposing LDS read ds_read_b64_tr_b16:
+//    within each group of 16 lanes, output lane i, element e is element
+//    i % 4 of source lane 4e + i / 4, so source lanes pointing at
+//    Wd[n0 + s/4][c0 + 4(s%4)] (s = lane % 16) hand lane i the four values
+//    Wd[n0 .. n0+3][c0 + i]; two reads give the 8 values of a fragment;
+//  * Wd's 16-byte chunk c of row n is stored at chunk c ^ swz(n), swz(n) =
+//    ((m & 1) << 2) | (m >> 1) with m = (n >> 1) & 7: the row-wise writes
+//    (16 rows, one chunk) and the transposing reads (4 rows, one aligned
+//    quad of chunks) both hit distinct 16-byte bank groups;
 //  * MFMA fragments as in the forward: lane-half h covers n in
 //    [32h, 32h + 32) of the step, sub-step kk the 8 values 32h + 8kk ..
 constexpr int kBwdBM = 128, kBwdBN = 256;
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+__device__ __forceinline__ int wd_swz(int n) {
+  const int m = (n >> 1) & 7;
+  return ((m & 1) << 2) | (m >> 1);
+}
+
 __global__ void __launch_bounds__(kGemmThreads, 2)
 k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ packed,
-                    const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
-                    int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out) {
+                 const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
+                 int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out) {
   constexpr int BM = kBwdBM, BN = kBwdBN, MT = BM / 32, NT = BN / 4 / 32;
   const int64_t col0 = (int64_t)blockIdx.x * BN;
   const TileInfo ti = find_tile<BM>(offs, experts, tokens, blockIdx.y);
@@ -534,19 +553,28 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
   }
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds_g[2][BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_wt[4][64 * 128];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_w[4][64 * 128];
 
   // grad_out staging: thread t owns chunks c = t + 256 i: row c / 8, chunk c % 8
+  const uint8_t* g_row[4];                             // start of the (clamped) row
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = threadIdx.x + i * kGemmThreads;
+    int64_t row = ti.row0 + (c >> 3);
+    if (row >= ti.row_end) row = ti.row_end - 1;       // never stored
+    g_row[i] = g + row * ndim * 2;
+  }
+  const int g_col = (threadIdx.x & 7) * 8;             // same chunk for all i (256 % 8 == 0)
   u32x4_t gr_regs[4];
   auto load_g = [&](int64_t n0) {
+    // n tail: chunks are 8-aligned and N % 8 == 0, so a chunk is wholly in or out;
+    // an out-of-range chunk reads the row's first chunk and is replaced by zeros
+    const bool ok = n0 + g_col < ndim;
+    const int64_t off = ok ? (n0 + g_col) * 2 : 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int c = threadIdx.x + i * kGemmThreads;
-      const int64_t row = ti.row0 + (c >> 3), n = n0 + (c & 7) * 8;
-      if (row < ti.row_end && n < ndim)
-        gr_regs[i] = *reinterpret_cast<const u32x4_t*>(g + (row * ndim + n) * 2);
-      else
-        gr_regs[i] = u32x4_t{0u, 0u, 0u, 0u};
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(g_row[i] + off);
+      gr_regs[i] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
     }
   };
   auto store_g = [&](uint8_t* dst) {
@@ -558,60 +586,50 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
     }
   };
 
-  // weight block of this lane: rows n0 + 8nb + i (i < 8), columns kcol .. kcol+7
-  const int nb = lane & 7, kb = lane >> 3;
-  const int64_t kcol = col0 + wave * 64 + kb * 8;
-  const bool kok = kcol < kdim;
-  const int64_t prow = kdim / 2, srow = kdim / 32;     // bytes per weight row (packed, scales)
-  const uint8_t* pbase = packed_e_of(packed, ti.expert, ndim, kdim) + (int64_t)nb * 8 * prow + kcol / 2;
-  const uint8_t* sbase = scales + (int64_t)ti.expert * ndim * srow + (int64_t)nb * 8 * srow + kcol / 32;
-  uint32_t pw[8], sw[8];
+  // weights: lane l takes row n0 + l, columns kc .. kc + 63 (two 16-byte halves)
+  const int64_t kc = col0 + wave * 64;
+  const bool v0 = kc + 32 <= kdim, v1 = kc + 64 <= kdim;   // K % 32 == 0: halves are all in or all out
+  const int64_t prow = kdim / 2, srow = kdim / 32;           // bytes per weight row (packed, scales)
+  const uint8_t* pe = packed_e_of(packed, ti.expert, ndim, kdim);
+  const uint8_t* se = scales + (int64_t)ti.expert * ndim * srow;
+  const int64_t off0 = v0 ? kc / 2 : 0, off1 = v1 ? kc / 2 + 16 : 0;
+  const int64_t soff0 = v0 ? kc / 32 : 0, soff1 = v1 ? kc / 32 + 1 : 0;
+  u32x4_t raw[2];
+  uint32_t sb[2];
   auto load_w = [&](int64_t n0) {
-    const uint8_t* pp = pbase + n0 * prow;
-    const uint8_t* sp = sbase + n0 * srow;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (kok && n0 + nb * 8 + i < ndim) {
-        pw[i] = *reinterpret_cast<const uint32_t*>(pp + i * prow);
-        sw[i] = sp[i * srow];
-      } else {
-        pw[i] = 0u;
-        sw[i] = 127u;
-      }
-    }
+    const int64_t n = n0 + lane;
+    const bool ok = n < ndim;
+    const int64_t nn = ok ? n : ndim - 1;
+    const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(pe + nn * prow + off0);
+    const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(pe + nn * prow + off1);
+    const uint32_t s0 = se[nn * srow + soff0], s1 = se[nn * srow + soff1];
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    raw[0] = ok && v0 ? a0 : z;
+    raw[1] = ok && v1 ? a1 : z;
+    sb[0] = ok && v0 ? s0 : 127u;     // rows / columns out of range decode to zeros
+    sb[1] = ok && v1 ? s1 : 127u;
   };
-  uint8_t* wt = lds_wt[wave];
-  auto build_wt = [&]() {
-    // two halves of 4 rows: decode, then regroup each output row's 4 n-values
+  uint8_t* wd = lds_w[wave];
+  auto build_wd = [&]() {
+    const int swz = wd_swz(lane);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      uint32_t d[4][4];   // d[row][pair q]: bf16 of k = 2q (lo), 2q+1 (hi)
+      const float sc = e8m0_to_f32(sb[half]);
+      const uint32_t w4[4] = {raw[half].x, raw[half].y, raw[half].z, raw[half].w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float sc = e8m0_to_f32(sw[4 * half + i]);
-        const uint32_t p = pw[4 * half + i];
-        d[i][0] = dec_fp4_bf16x2<0>(p, sc);
-        d[i][1] = dec_fp4_bf16x2<1>(p, sc);
-        d[i][2] = dec_fp4_bf16x2<2>(p, sc);
-        d[i][3] = dec_fp4_bf16x2<3>(p, sc);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        // Wt row k = 8kb + jj, logical chunk nb, 8-byte half `half`.  Lanes with
-        // odd kb write the rows of each pair in swapped order (jj = j ^ 1), so
-        // one instruction writes rows of both parities, i.e. both 128-byte
-        // halves of the 256-byte bank space (LDS takes 32 lanes x 8 bytes per
-        // cycle), instead of piling into one.
-        const int jj = j ^ (kb & 1);
-        const uint32_t sel = (jj & 1) ? 0x07060302u : 0x05040100u;
-        u32x2_t o;
-        o.x = __builtin_amdgcn_perm(d[1][j >> 1], d[0][j >> 1], sel);
-        o.y = __builtin_amdgcn_perm(d[3][j >> 1], d[2][j >> 1], sel);
-        const int k = kb * 8 + jj;
-        *reinterpret_cast<u32x2_t*>(wt + k * 128 + 16 * (nb ^ ((k >> 1) & 7)) + 8 * half) = o;
+      for (int q = 0; q < 4; ++q) {
+        const u32x4_t v = {dec_fp4_bf16x2<0>(w4[q], sc), dec_fp4_bf16x2<1>(w4[q], sc), dec_fp4_bf16x2<2>(w4[q], sc),
+                           dec_fp4_bf16x2<3>(w4[q], sc)};
+        const int chunk = 4 * half + q;   // columns 8 chunk .. 8 chunk + 7
+        *reinterpret_cast<u32x4_t*>(wd + lane * 128 + 16 * (chunk ^ swz)) = v;
       }
     }
   };
+  // transposing-read addresses: group gq = lane / 16 -> h = gq / 2, column
+  // half gq % 2; source lane s = lane % 16 -> row a = s / 4, columns 4 (s % 4)
+  const int gq = lane >> 4, sl = lane & 15;
+  const int tr_row = 32 * (gq >> 1) + (sl >> 2);          // + 8 kk (+ 4)
+  const int tr_col = 16 * (gq & 1) + 4 * (sl & 3);        // + 32 j
 
   f32x16_t acc[MT][NT];
 #pragma unroll
@@ -625,24 +643,33 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
   store_g(lds_g[0]);
   __syncthreads();
 
-  const int swz = (r >> 1) & 7;
+  const int swz_g = (r >> 1) & 7;
   for (int s = 0; s < nsteps; ++s) {
     const int cur = s & 1;
-    build_wt();                                   // this step's weights -> this wave's Wt
+    build_wd();                                   // this step's weights -> this wave's Wd
     if (s + 1 < nsteps) {
       load_g((int64_t)(s + 1) * kBK);
       load_w((int64_t)(s + 1) * kBK);
     }
     const uint8_t* la = lds_g[cur] + r * 128;
-    const uint8_t* lb = wt + r * 128;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int off = 16 * ((4 * h + kk) ^ swz);
+      const int off = 16 * ((4 * h + kk) ^ swz_g);
       bf16x8_t fa[MT], fb[NT];
 #pragma unroll
       for (int i = 0; i < MT; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(la + i * 32 * 128 + off);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) fb[j] = *reinterpret_cast<const bf16x8_t*>(lb + j * 32 * 128 + off);
+      for (int j = 0; j < NT; ++j) {
+        const int col = tr_col + 32 * j;
+        v4i16_t t[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int n = tr_row + 8 * kk + 4 * u;
+          const uint8_t* src = wd + n * 128 + 16 * ((col >> 3) ^ wd_swz(n)) + 2 * (col & 7);
+          t[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(src));
+        }
+        fb[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
