@@ -569,12 +569,15 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
   auto load_g = [&](int64_t n0) {
     // n tail: chunks are 8-aligned and N % 8 == 0, so a chunk is wholly in or out;
     // an out-of-range chunk reads the row's first chunk and is replaced by zeros
+    // (a mask, not a select: the compiler would turn a select into a branch
+    // around the load, whose join then waits for every load in flight)
     const bool ok = n0 + g_col < ndim;
     const int64_t off = ok ? (n0 + g_col) * 2 : 0;
+    const uint32_t m = ok ? ~0u : 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const u32x4_t v = *reinterpret_cast<const u32x4_t*>(g_row[i] + off);
-      gr_regs[i] = ok ? v : u32x4_t{0u, 0u, 0u, 0u};
+      gr_regs[i] = v & m;
     }
   };
   auto store_g = [&](uint8_t* dst) {
@@ -603,11 +606,13 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
     const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(pe + nn * prow + off0);
     const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(pe + nn * prow + off1);
     const uint32_t s0 = se[nn * srow + soff0], s1 = se[nn * srow + soff1];
-    const u32x4_t z = {0u, 0u, 0u, 0u};
-    raw[0] = ok && v0 ? a0 : z;
-    raw[1] = ok && v1 ? a1 : z;
-    sb[0] = ok && v0 ? s0 : 127u;     // rows / columns out of range decode to zeros
-    sb[1] = ok && v1 ? s1 : 127u;
+    // rows / columns out of range decode to zeros (code 0, scale byte 127);
+    // masks rather than selects keep the loads unconditional
+    const uint32_t m0 = ok && v0 ? ~0u : 0u, m1 = ok && v1 ? ~0u : 0u;
+    raw[0] = a0 & m0;
+    raw[1] = a1 & m1;
+    sb[0] = (s0 & m0) | (127u & ~m0);
+    sb[1] = (s1 & m1) | (127u & ~m1);
   };
   uint8_t* wd = lds_w[wave];
   auto build_wd = [&]() {
@@ -651,6 +656,7 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
       load_g((int64_t)(s + 1) * kBK);
       load_w((int64_t)(s + 1) * kBK);
     }
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the MFMAs
     const uint8_t* la = lds_g[cur] + r * 128;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
