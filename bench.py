@@ -265,9 +265,11 @@ def main():
         achieved, peak, unit, bound = work_per_launch / (avg_launch_ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
     else:
         achieved, peak, unit, bound = work_per_launch / (avg_launch_ms * 1e-3) / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
+    traffic = measured_traffic(dom_name)
     roofline = {"bound": bound, "kernel": dom_name, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "avg_launch_us": round(avg_launch_ms * 1e3, 1),
-                "work_per_launch": work_per_launch, "traffic": measured_traffic(dom_name)}
+                "work_per_launch": work_per_launch,
+                "traffic": traffic["bytes_per_launch"] if traffic else None, "traffic_detail": traffic}
 
     cpu = None
     if not args.no_cpu_baseline and moe is not None:
@@ -307,9 +309,10 @@ def main():
 
 
 def measured_traffic(kernel):
-    """HBM-side bytes per launch of `kernel` from the committed counter summary
-    (rocprofv3 FETCH_SIZE and WRITE_SIZE, calibrated on the copy kernel), or
-    None when there is none or the kernel source changed since it was taken."""
+    """Bytes per launch of `kernel` past L2 (to Infinity Cache / HBM) from the
+    committed counter summary (rocprofv3 FETCH_SIZE and WRITE_SIZE, scaled by
+    what they read for the copy kernel), averaged over the launches the bench
+    makes, or None when there is none or the kernel source changed since."""
     import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", "traffic.json")
@@ -325,7 +328,8 @@ def measured_traffic(kernel):
         if hashlib.sha256(f.read()).hexdigest() != k["source_sha256"]:
             return None
     return {"bytes_per_launch": k["bytes_per_launch"], "fetch_bytes": k["fetch_bytes"],
-            "write_bytes": k["write_bytes"], "calibration": rec.get("calibration"), "from": "profiles/traffic.json"}
+            "write_bytes": k["write_bytes"], "unit": "bytes",
+            "fetch_factor": rec.get("calibration", {}).get("fetch_factor"), "from": "profiles/traffic.json"}
 
 
 def cpu_baseline(moe):
