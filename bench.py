@@ -19,7 +19,9 @@ workload, all inputs already resident in HBM:
 
 Legs whose working set fits in the 256 MB Infinity Cache rotate over enough
 buffer copies to exceed it.  Each leg is bracketed by HIP events recorded on
-the stream its kernels run on; `value` is the grouped-GEMM throughput of the
+the stream its kernels run on; a leg of short calls repeats them over
+rotating inputs (32 calls per step for the KV cache) so that the hand-over
+from the previous leg is a small share of its time; `value` is the grouped-GEMM throughput of the
 routed-expert layer (algorithmic flops 2 * rows * N * K summed over its four
 GEMMs, divided by their event time); `hbm` aggregates the codec legs
 (algorithmic bytes over event time).  Prints one JSON line.
@@ -140,27 +142,29 @@ def main():
                                          2048, e8_o.data_ptr(), e8_y[j].data_ptr(), sp), "e8 fwd")
         legs.append(Leg("e8.fwd", "k_grouped_mm_fwd_dma", "flop", 2.0 * 4096 * 2048 * 4096, e8_fn, reps=R8))
 
-    # ---------------- KV cache quantize_cache x3 + STE (8 rotating sets: 8 x 64 MiB per leg)
+    # ---------------- KV cache quantize_cache x3 + STE: 32 calls per step over 16 rotating sets of
+    # 32 MiB in + 32 MiB out (537 MB of inputs per leg, twice the Infinity Cache), separate inputs per
+    # leg, so no call reads what an earlier one left in the cache
     if wanted("kv"):
         kv = synth.kv_cache(seed=0)
-        R = 8
-        kv_x = [bf16(kv["x"]) for _ in range(R)]
-        kv_o = [torch.empty_like(kv_x[0]) for _ in range(R)]
+        R, KV_REPS = 16, 32
+        kv_xs = {fmt: [bf16(kv["x"]) for _ in range(R)] for fmt in ("fp8", "mxfp4", "nvfp4")}
+        kv_o = [torch.empty_like(kv_xs["fp8"][0]) for _ in range(R)]
         kv_g = [bf16(kv["grad"]) for _ in range(R)]
         kv_gi = [torch.empty_like(kv_g[0]) for _ in range(R)]
-        n_kv = kv_x[0].numel()
+        n_kv = kv_o[0].numel()
         rows_kv, C_kv = n_kv // 512, 512
         for fmt, code, block in [("fp8", 0, 128), ("mxfp4", 1, 32), ("nvfp4", 2, 16)]:
-            def f(i, code=code, block=block):
+            def f(i, code=code, block=block, kv_x=kv_xs[fmt]):
                 j = i % R
                 check(L.quantize_cache(kv_x[j].data_ptr(), kv_o[j].data_ptr(), 1, rows_kv, C_kv, code, block, sp), "kv")
             legs.append(Leg(f"kv.quantize_cache.{fmt}", f"k_quantize_cache<bf16,{fmt},{block // 8}>", "byte",
-                            4.0 * n_kv, f, reps=R))
+                            4.0 * n_kv, f, reps=KV_REPS))
 
         def ste(i):
             j = i % R
             check(L.quantize_cache_bwd(kv_g[j].data_ptr(), kv_gi[j].data_ptr(), 1, n_kv, sp), "ste")
-        legs.append(Leg("kv.ste_bwd", "k_copy16", "byte", 4.0 * n_kv, ste, reps=R))
+        legs.append(Leg("kv.ste_bwd", "k_copy16", "byte", 4.0 * n_kv, ste, reps=KV_REPS))
 
     # ---------------- bulk bf16 [65536, 7168] + 2^30-parameter weight dequant
     if wanted("bulk"):

@@ -18,27 +18,38 @@ namespace mxq {
 constexpr int kThreads = 256;
 constexpr int kGridCap = 16384;   // workgroups of a grid-stride launch (64 per CU)
 
-// Access mode of a streaming launch, chosen on the host by input size (MI355X
-// measurements): inputs larger than the 256 MB Infinity Cache stream best with
-// non-temporal loads and 8 chunks in flight per lane; smaller ones with plain
-// loads and 4.
-#ifndef MXQ_SMALL_NT_STORE
-#define MXQ_SMALL_NT_STORE 1
-#endif
+// Access mode of a streaming launch, chosen on the host (MI355X measurements
+// on data not in any cache).  Inputs of 256 MB and more: 8 chunks in flight
+// per lane, non-temporal loads and stores.  Quantizers on smaller inputs (a
+// 67 MB KV cache): 16 chunks per lane, so the whole input is requested in one
+// round by half as many waves (~6% faster there, ~4% slower on large inputs).
+// The copy of the straight-through backward streams best with the large-input
+// mode at any size (16 chunks per lane: -20%).
 struct StreamBig {
   static constexpr int kUnroll = 8;
   template <typename T> __device__ static __forceinline__ T ld(const T* p) { return __builtin_nontemporal_load(p); }
   template <typename T> __device__ static __forceinline__ void st(T v, T* p) { __builtin_nontemporal_store(v, p); }
 };
+// Quantizer inputs below 16 MB: one chunk per lane (16 per lane would leave
+// a handful of workgroups for the whole GPU).
+struct StreamTiny {
+  static constexpr int kUnroll = 1;
+  template <typename T> __device__ static __forceinline__ T ld(const T* p) { return *p; }
+  template <typename T> __device__ static __forceinline__ void st(T v, T* p) { __builtin_nontemporal_store(v, p); }
+};
 struct StreamSmall {
+  static constexpr int kUnroll = 16;
+  template <typename T> __device__ static __forceinline__ T ld(const T* p) { return __builtin_nontemporal_load(p); }
+  template <typename T> __device__ static __forceinline__ void st(T v, T* p) { __builtin_nontemporal_store(v, p); }
+};
+// Dequantization (all sizes): plain loads of the packed bytes, 4 chunks per
+// lane, non-temporal stores of the 4x larger output.
+struct StreamDequant {
   static constexpr int kUnroll = 4;
   template <typename T> __device__ static __forceinline__ T ld(const T* p) { return *p; }
-  template <typename T> __device__ static __forceinline__ void st(T v, T* p) {
-    if constexpr (MXQ_SMALL_NT_STORE) __builtin_nontemporal_store(v, p);
-    else *p = v;
-  }
+  template <typename T> __device__ static __forceinline__ void st(T v, T* p) { __builtin_nontemporal_store(v, p); }
 };
-constexpr int64_t kBigStreamBytes = 256ll << 20;
+constexpr int64_t kBigStreamBytes = 256ll << 20, kTinyStreamBytes = 16ll << 20;
 
 template <int DT>
 struct Chunk {
@@ -388,8 +399,8 @@ __global__ void __launch_bounds__(kThreads) k_zero_bytes(uint8_t* __restrict__ d
 
 // ------------------------------------------------------------------ launchers
 static inline int grid_for(int64_t items, int64_t per_block) {
-  int64_t g = (items + per_block - 1) / per_block;
   const int64_t cap = kGridCap;
+  int64_t g = (items + per_block - 1) / per_block;
   return (int)(g < 1 ? 1 : (g > cap ? cap : g));
 }
 static inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -399,12 +410,15 @@ static hipError_t launch_quantize_mxfp4_t(const void* x, int64_t rows, int64_t k
                                           hipStream_t st) {
   const int64_t n = rows * k;
   if (aligned(x, 16) && aligned(packed, 4)) {
-    const int64_t nchunks = n / 8;
-    if (n * (DT == DT_F32 ? 4 : 2) >= kBigStreamBytes)
+    const int64_t nchunks = n / 8, bytes = n * (DT == DT_F32 ? 4 : 2);
+    if (bytes >= kBigStreamBytes)
       hipLaunchKernelGGL((k_quantize_mxfp4<DT, StreamBig>), dim3(grid_for(nchunks, kThreads * StreamBig::kUnroll)),
                          dim3(kThreads), 0, st, (const uint8_t*)x, (uint32_t*)packed, scales, nchunks);
-    else
+    else if (bytes >= kTinyStreamBytes)
       hipLaunchKernelGGL((k_quantize_mxfp4<DT, StreamSmall>), dim3(grid_for(nchunks, kThreads * StreamSmall::kUnroll)),
+                         dim3(kThreads), 0, st, (const uint8_t*)x, (uint32_t*)packed, scales, nchunks);
+    else
+      hipLaunchKernelGGL((k_quantize_mxfp4<DT, StreamTiny>), dim3(grid_for(nchunks, kThreads * StreamTiny::kUnroll)),
                          dim3(kThreads), 0, st, (const uint8_t*)x, (uint32_t*)packed, scales, nchunks);
   } else {
     const int64_t nb = n / 32;
@@ -431,7 +445,7 @@ static hipError_t launch_dequantize_mxfp4_t(const int8_t* packed, const uint8_t*
     // dequantization is write-dominated (1 packed byte -> 4..8 output bytes):
     // plain loads measured best at every size
     const int64_t nchunks = n / 8;
-    hipLaunchKernelGGL((k_dequantize_mxfp4<DT, StreamSmall>), dim3(grid_for(nchunks, kThreads * StreamSmall::kUnroll)),
+    hipLaunchKernelGGL((k_dequantize_mxfp4<DT, StreamDequant>), dim3(grid_for(nchunks, kThreads * StreamDequant::kUnroll)),
                        dim3(kThreads), 0, st, (const uint32_t*)packed, scales, (uint8_t*)out, nchunks);
   } else {
     const int64_t nb = n / 32;
@@ -452,12 +466,17 @@ hipError_t launch_dequantize_mxfp4(const int8_t* packed, const uint8_t* scales, 
 
 template <int DT, int FMT, int L>
 static void launch_cache_fast(const void* x, void* out, int64_t nchunks, hipStream_t st) {
-  if (nchunks * 8 * (DT == DT_F32 ? 4 : 2) >= kBigStreamBytes)
+  const int64_t bytes = nchunks * 8 * (DT == DT_F32 ? 4 : 2);
+  if (bytes >= kBigStreamBytes)
     hipLaunchKernelGGL((k_quantize_cache<DT, FMT, L, StreamBig>), dim3(grid_for(nchunks, kThreads * StreamBig::kUnroll)),
                        dim3(kThreads), 0, st, (const uint8_t*)x, (uint8_t*)out, nchunks);
-  else
+  else if (bytes >= kTinyStreamBytes)
     hipLaunchKernelGGL((k_quantize_cache<DT, FMT, L, StreamSmall>),
                        dim3(grid_for(nchunks, kThreads * StreamSmall::kUnroll)), dim3(kThreads), 0, st,
+                       (const uint8_t*)x, (uint8_t*)out, nchunks);
+  else
+    hipLaunchKernelGGL((k_quantize_cache<DT, FMT, L, StreamTiny>),
+                       dim3(grid_for(nchunks, kThreads * StreamTiny::kUnroll)), dim3(kThreads), 0, st,
                        (const uint8_t*)x, (uint8_t*)out, nchunks);
 }
 
@@ -506,12 +525,8 @@ hipError_t launch_quantize_cache(const void* x, void* out, int dt, int64_t rows,
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st) {
   if (aligned(src, 16) && aligned(dst, 16) && bytes % 16 == 0) {
     const int64_t n16 = bytes / 16;
-    if (bytes >= kBigStreamBytes)
-      hipLaunchKernelGGL(k_copy16<StreamBig>, dim3(grid_for(n16, kThreads * StreamBig::kUnroll)), dim3(kThreads), 0,
-                         st, (const u32x4_t*)src, (u32x4_t*)dst, n16);
-    else
-      hipLaunchKernelGGL(k_copy16<StreamSmall>, dim3(grid_for(n16, kThreads * StreamSmall::kUnroll)), dim3(kThreads),
-                         0, st, (const u32x4_t*)src, (u32x4_t*)dst, n16);
+    hipLaunchKernelGGL(k_copy16<StreamBig>, dim3(grid_for(n16, kThreads * StreamBig::kUnroll)), dim3(kThreads), 0,
+                       st, (const u32x4_t*)src, (u32x4_t*)dst, n16);
   } else {
     hipLaunchKernelGGL(k_copy_bytes, dim3(grid_for(bytes, kThreads * 4)), dim3(kThreads), 0, st,
                        (const uint8_t*)src, (uint8_t*)dst, bytes);

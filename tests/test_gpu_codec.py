@@ -191,6 +191,29 @@ def test_bulk_stream_mxfp4_sampled_rows():
         assert_bits_equal(from_gpu_bits(out[ri]), oracle.quantize_cache(x, fmt, block, "bf16"), f"cache {fmt}")
 
 
+@pytest.mark.parametrize("dtype,rows,cols", [("bf16", 8192, 4096), ("f32", 4096, 2048), ("f16", 2048, 8192)])
+def test_mid_size_inputs_sampled_rows(dtype, rows, cols):
+    """33-67 MB inputs (between the tiny and the large-input access modes):
+    quantize_mxfp4 + dequantize and quantize_cache in three formats, 64 sampled
+    rows against the oracle."""
+    g = np.random.default_rng(rows + cols)
+    x32 = (g.standard_normal((rows, cols)) * np.exp2(g.integers(-4, 5, (rows, 1)))).astype(np.float32)
+    bits = bits_of(x32, dtype)
+    t = to_gpu_bits(bits, dtype)
+    sel = np.sort(g.choice(rows, 64, replace=False))
+    ri = torch.from_numpy(sel).to(dev())
+    x = oracle.from_dtype_bits(bits[sel], dtype)
+    p, s = mxq.quantize_mxfp4(t)
+    wp, ws = oracle.quantize_mxfp4(x)
+    assert_bits_equal(from_gpu_bits(p[ri]).view(np.uint8), wp.view(np.uint8), f"packed {dtype}")
+    assert_bits_equal(from_gpu_bits(s[ri]), ws, f"scales {dtype}")
+    back = mxq.dequantize_mxfp4(p, s, t.dtype)
+    assert_bits_equal(from_gpu_bits(back[ri]), oracle.dequantize_mxfp4(wp, ws, dtype), f"dequant {dtype}")
+    for fmt, block in [("fp8", 128), ("mxfp4", 32), ("nvfp4", 16)]:
+        out = mxq.quantize_cache(t, fmt, block)
+        assert_bits_equal(from_gpu_bits(out[ri]), oracle.quantize_cache(x, fmt, block, dtype), f"cache {fmt} {dtype}")
+
+
 # ------------------------------------------------------------- quantize_cache
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "nvfp4"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
