@@ -23,8 +23,6 @@ constexpr int kGridCap = 16384;   // workgroups of a grid-stride launch (64 per 
 // per lane, non-temporal loads and stores.  Quantizers on smaller inputs (a
 // 67 MB KV cache): 16 chunks per lane, so the whole input is requested in one
 // round by half as many waves (~6% faster there, ~4% slower on large inputs).
-// The copy of the straight-through backward streams best with the large-input
-// mode at any size (16 chunks per lane: -20%).
 struct StreamBig {
   static constexpr int kUnroll = 8;
   template <typename T> __device__ static __forceinline__ T ld(const T* p) { return __builtin_nontemporal_load(p); }
@@ -42,11 +40,11 @@ struct StreamSmall {
   template <typename T> __device__ static __forceinline__ T ld(const T* p) { return __builtin_nontemporal_load(p); }
   template <typename T> __device__ static __forceinline__ void st(T v, T* p) { __builtin_nontemporal_store(v, p); }
 };
-// Dequantization (all sizes): plain loads of the packed bytes, 4 chunks per
-// lane, non-temporal stores of the 4x larger output.
+// Dequantization (all sizes): 4 chunks per lane, non-temporal loads of the
+// packed bytes and stores of the 4x larger output.
 struct StreamDequant {
   static constexpr int kUnroll = 4;
-  template <typename T> __device__ static __forceinline__ T ld(const T* p) { return *p; }
+  template <typename T> __device__ static __forceinline__ T ld(const T* p) { return __builtin_nontemporal_load(p); }
   template <typename T> __device__ static __forceinline__ void st(T v, T* p) { __builtin_nontemporal_store(v, p); }
 };
 constexpr int64_t kBigStreamBytes = 256ll << 20, kTinyStreamBytes = 16ll << 20;
@@ -368,21 +366,23 @@ __global__ void __launch_bounds__(kThreads) k_quantize_cache_general(const uint8
 }
 
 // ------------------------------------------------------------ STE copy
-template <class M>
-__global__ void __launch_bounds__(kThreads) k_copy16(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
-                                                   int64_t n16) {
-  const int64_t step = (int64_t)gridDim.x * kThreads * M::kUnroll;
-  for (int64_t base = (int64_t)blockIdx.x * kThreads * M::kUnroll; base < n16; base += step) {
-    u32x4_t v[M::kUnroll];
+// 1024-thread workgroups, 4 x 16 bytes per lane, non-temporal both ways
+// (measured best at every size: 256 threads x 8 chunks is ~6% slower).
+constexpr int kCopyThreads = 1024, kCopyUnroll = 4;
+__global__ void __launch_bounds__(kCopyThreads) k_copy16(const u32x4_t* __restrict__ src, u32x4_t* __restrict__ dst,
+                                                       int64_t n16) {
+  const int64_t step = (int64_t)gridDim.x * kCopyThreads * kCopyUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kCopyThreads * kCopyUnroll; base < n16; base += step) {
+    u32x4_t v[kCopyUnroll];
 #pragma unroll
-    for (int u = 0; u < M::kUnroll; ++u) {
-      const int64_t i = base + u * kThreads + threadIdx.x;
-      if (i < n16) v[u] = M::ld(src + i);
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = base + u * kCopyThreads + threadIdx.x;
+      if (i < n16) v[u] = __builtin_nontemporal_load(src + i);
     }
 #pragma unroll
-    for (int u = 0; u < M::kUnroll; ++u) {
-      const int64_t i = base + u * kThreads + threadIdx.x;
-      if (i < n16) M::st(v[u], dst + i);
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t i = base + u * kCopyThreads + threadIdx.x;
+      if (i < n16) __builtin_nontemporal_store(v[u], dst + i);
     }
   }
 }
@@ -525,8 +525,8 @@ hipError_t launch_quantize_cache(const void* x, void* out, int dt, int64_t rows,
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st) {
   if (aligned(src, 16) && aligned(dst, 16) && bytes % 16 == 0) {
     const int64_t n16 = bytes / 16;
-    hipLaunchKernelGGL(k_copy16<StreamBig>, dim3(grid_for(n16, kThreads * StreamBig::kUnroll)), dim3(kThreads), 0,
-                       st, (const u32x4_t*)src, (u32x4_t*)dst, n16);
+    hipLaunchKernelGGL(k_copy16, dim3(grid_for(n16, kCopyThreads * kCopyUnroll)), dim3(kCopyThreads), 0, st,
+                       (const u32x4_t*)src, (u32x4_t*)dst, n16);
   } else {
     hipLaunchKernelGGL(k_copy_bytes, dim3(grid_for(bytes, kThreads * 4)), dim3(kThreads), 0, st,
                        (const uint8_t*)src, (uint8_t*)dst, bytes);
