@@ -533,7 +533,8 @@ __global__ void __launch_bounds__(kGemmThreads, 2)
 k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ packed,
                  const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
                  int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out) {
-  constexpr int BM = kBwdBM, BN = kBwdBN, MT = BM / 32, NT = BN / 4 / 32;
+  constexpr int BM = kBwdBM, BN = kBwdBN, MT = BM / 32, NT = 2, kThreads = kGemmThreads;
+  constexpr int GC = BM * 8 / kThreads;                // 16-byte grad_out chunks per thread and step
   const int64_t col0 = (int64_t)blockIdx.x * BN;
   const TileInfo ti = find_tile<BM>(offs, experts, tokens, blockIdx.y);
   if (ti.expert == -2) return;
@@ -541,7 +542,7 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
   const int h = lane >> 5, r = lane & 31;
 
   if (ti.expert == -1) {
-    for (int i = threadIdx.x; i < BM * BN / 8; i += kGemmThreads) {
+    for (int i = threadIdx.x; i < BM * BN / 8; i += kThreads) {
       const int rr = i / (BN / 8), c = (i % (BN / 8)) * 8;
       const int64_t gr = ti.row0 + rr, gc = col0 + c;
       if (gr < ti.row_end && gc < kdim) {
@@ -556,36 +557,36 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
   __shared__ __attribute__((aligned(1024))) uint8_t lds_w[4][64 * 128];
 
   // grad_out staging: thread t owns chunks c = t + 256 i: row c / 8, chunk c % 8
-  const uint8_t* g_row[4];                             // start of the (clamped) row
+  const uint8_t* g_row[GC];                            // start of the (clamped) row
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = threadIdx.x + i * kGemmThreads;
+  for (int i = 0; i < GC; ++i) {
+    const int c = threadIdx.x + i * kThreads;
     int64_t row = ti.row0 + (c >> 3);
     if (row >= ti.row_end) row = ti.row_end - 1;       // never stored
     g_row[i] = g + row * ndim * 2;
   }
-  const int g_col = (threadIdx.x & 7) * 8;             // same chunk for all i (256 % 8 == 0)
-  u32x4_t gr_regs[4];
+  const int g_col = (threadIdx.x & 7) * 8;             // same chunk for all i
+  // Loads are unconditional (clamped addresses) and their values are masked
+  // only where they are consumed: a select next to a load becomes a branch
+  // around it, and a mask next to it inside a conditional block makes the
+  // compiler wait for the load right there.
+  u32x4_t gr_regs[GC];
+  uint32_t g_mask = 0;
   auto load_g = [&](int64_t n0) {
     // n tail: chunks are 8-aligned and N % 8 == 0, so a chunk is wholly in or out;
-    // an out-of-range chunk reads the row's first chunk and is replaced by zeros
-    // (a mask, not a select: the compiler would turn a select into a branch
-    // around the load, whose join then waits for every load in flight)
+    // an out-of-range chunk reads the row's first chunk and is zeroed
     const bool ok = n0 + g_col < ndim;
     const int64_t off = ok ? (n0 + g_col) * 2 : 0;
-    const uint32_t m = ok ? ~0u : 0u;
+    g_mask = ok ? ~0u : 0u;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(g_row[i] + off);
-      gr_regs[i] = v & m;
-    }
+    for (int i = 0; i < GC; ++i) gr_regs[i] = *reinterpret_cast<const u32x4_t*>(g_row[i] + off);
   };
   auto store_g = [&](uint8_t* dst) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = threadIdx.x + i * kGemmThreads;
+    for (int i = 0; i < GC; ++i) {
+      const int c = threadIdx.x + i * kThreads;
       const int row = c >> 3, chunk = c & 7;
-      *reinterpret_cast<u32x4_t*>(dst + row * 128 + 16 * (chunk ^ ((row >> 1) & 7))) = gr_regs[i];
+      *reinterpret_cast<u32x4_t*>(dst + row * 128 + 16 * (chunk ^ ((row >> 1) & 7))) = gr_regs[i] & g_mask;
     }
   };
 
@@ -598,29 +599,27 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
   const int64_t off0 = v0 ? kc / 2 : 0, off1 = v1 ? kc / 2 + 16 : 0;
   const int64_t soff0 = v0 ? kc / 32 : 0, soff1 = v1 ? kc / 32 + 1 : 0;
   u32x4_t raw[2];
-  uint32_t sb[2];
+  uint32_t sb[2], wm[2];
   auto load_w = [&](int64_t n0) {
     const int64_t n = n0 + lane;
     const bool ok = n < ndim;
     const int64_t nn = ok ? n : ndim - 1;
-    const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(pe + nn * prow + off0);
-    const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(pe + nn * prow + off1);
-    const uint32_t s0 = se[nn * srow + soff0], s1 = se[nn * srow + soff1];
-    // rows / columns out of range decode to zeros (code 0, scale byte 127);
-    // masks rather than selects keep the loads unconditional
-    const uint32_t m0 = ok && v0 ? ~0u : 0u, m1 = ok && v1 ? ~0u : 0u;
-    raw[0] = a0 & m0;
-    raw[1] = a1 & m1;
-    sb[0] = (s0 & m0) | (127u & ~m0);
-    sb[1] = (s1 & m1) | (127u & ~m1);
+    raw[0] = *reinterpret_cast<const u32x4_t*>(pe + nn * prow + off0);
+    raw[1] = *reinterpret_cast<const u32x4_t*>(pe + nn * prow + off1);
+    sb[0] = se[nn * srow + soff0];
+    sb[1] = se[nn * srow + soff1];
+    // rows / columns out of range decode to zeros (code 0, scale byte 127)
+    wm[0] = ok && v0 ? ~0u : 0u;
+    wm[1] = ok && v1 ? ~0u : 0u;
   };
   uint8_t* wd = lds_w[wave];
   auto build_wd = [&]() {
     const int swz = wd_swz(lane);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const float sc = e8m0_to_f32(sb[half]);
-      const uint32_t w4[4] = {raw[half].x, raw[half].y, raw[half].z, raw[half].w};
+      const float sc = e8m0_to_f32((sb[half] & wm[half]) | (127u & ~wm[half]));
+      const u32x4_t p = raw[half] & wm[half];
+      const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const u32x4_t v = {dec_fp4_bf16x2<0>(w4[q], sc), dec_fp4_bf16x2<1>(w4[q], sc), dec_fp4_bf16x2<2>(w4[q], sc),
@@ -652,10 +651,9 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
   for (int s = 0; s < nsteps; ++s) {
     const int cur = s & 1;
     build_wd();                                   // this step's weights -> this wave's Wd
-    if (s + 1 < nsteps) {
-      load_g((int64_t)(s + 1) * kBK);
-      load_w((int64_t)(s + 1) * kBK);
-    }
+    // the next step's loads (clamped at the end: in range, never used)
+    load_g((int64_t)min(s + 1, nsteps - 1) * kBK);
+    load_w((int64_t)min(s + 1, nsteps - 1) * kBK);
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the MFMAs
     const uint8_t* la = lds_g[cur] + r * 128;
 #pragma unroll
@@ -682,7 +680,11 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
         for (int j = 0; j < NT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (s + 1 < nsteps) store_g(lds_g[cur ^ 1]);
+    // unconditional (the last step stores a clamped copy nobody reads): a
+    // conditional store would let the compiler sink the loads into its block;
+    // the barrier keeps the masking of the loaded values after the MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+    store_g(lds_g[cur ^ 1]);
     __syncthreads();
   }
 
@@ -690,7 +692,7 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
   for (int i = 0; i < MT; ++i) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int64_t gc = col0 + wave * (BN / 4) + j * 32 + r;
+      const int64_t gc = col0 + wave * 64 + j * 32 + r;
 #pragma unroll
       for (int q = 0; q < 16; q += 2) {
         const int64_t gr0 = ti.row0 + i * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
