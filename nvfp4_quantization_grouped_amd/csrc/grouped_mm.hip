@@ -715,15 +715,11 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
     const int64_t gx = (wn_dim + kFwdBN - 1) / kFwdBN;
     const int64_t gy = (tokens + kFwdBM - 1) / kFwdBM + experts;
     if (wk_dim % 128 == 0 && ((uintptr_t)scales & 3) == 0) {
-#ifndef MXQ_FWD_WIDE
-#define MXQ_FWD_WIDE 1
-#endif
-#ifndef MXQ_FWD_SCH8
-#define MXQ_FWD_SCH8 1
-#endif
-      const bool sch8 = MXQ_FWD_SCH8 && wk_dim % 512 == 0 && ((uintptr_t)scales & 15) == 0;
+      // scale bytes in 8-step chunks when whole chunks exist (16-byte aligned
+      // rows); 128 x 512 tiles (8 waves) when they still give two per CU
+      const bool sch8 = wk_dim % 512 == 0 && ((uintptr_t)scales & 15) == 0;
       const int64_t gx8 = (wn_dim + 511) / 512;
-      const bool wide = MXQ_FWD_WIDE && gx8 * gy >= 2 * 256;
+      const bool wide = gx8 * gy >= 2 * 256;
       const dim3 g4((unsigned)gx, (unsigned)gy), g8((unsigned)gx8, (unsigned)gy);
 #define MXQ_FWD_LAUNCH(W, ST, WG, SCH, G)                                                                    \
   hipLaunchKernelGGL((k_grouped_mm_fwd_dma<W, ST, WG, SCH>), G, dim3(W * 64), 0, st, (const uint8_t*)a,      \
