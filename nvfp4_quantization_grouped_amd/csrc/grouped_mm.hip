@@ -310,24 +310,30 @@ struct DmaSmem<W, STAGES, 2> {
   Stage st[STAGES];
 };
 
-// One step's activation and weight transfers of one wave, straight into LDS
-// (plus the per-step scale dword when SCH == 2).
-template <int W, int STAGES, int SCH>
-__device__ __forceinline__ void fwd_dma_issue(typename DmaSmem<W, STAGES, SCH>::Stage& d,
-                                              const uint8_t* const (&a_src)[16 / W],
-                                              const uint8_t* const (&b_src)[2], const uint8_t* s_src, int wave,
-                                              int step) {
-  constexpr int QA = DmaSmem<W, STAGES, SCH>::kABlocksPerWave;
-  const int64_t ka = (int64_t)step * kBK * 2;     // activation bytes
-  const int64_t kb = (int64_t)step * 32;          // packed bytes
-#pragma unroll
-  for (int q = 0; q < QA; ++q)
-    __builtin_amdgcn_global_load_lds(a_src[q] + ka, (lds_void_t*)(d.a + 1024 * (QA * wave + q)), 16, 0, 0);
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-    __builtin_amdgcn_global_load_lds(b_src[j] + kb, (lds_void_t*)(d.b + 2048 * wave + 1024 * j), 16, 0, 0);
-  if constexpr (SCH == 2)
+// Op q of one step's transfers of one wave, straight into LDS (q < QA:
+// activation block q; then the 2 weight blocks; then, with SCH == 2, the
+// scale dword).
+template <int QA, int SCH, class StageT>
+__device__ __forceinline__ void fwd_dma_op(StageT& d, const uint8_t* const* a_src, const uint8_t* const* b_src,
+                                           const uint8_t* s_src, int wave, int step, int q) {
+  if (q < QA) {
+    __builtin_amdgcn_global_load_lds(a_src[q] + (int64_t)step * kBK * 2, (lds_void_t*)(d.a + 1024 * (QA * wave + q)),
+                                     16, 0, 0);
+  } else if (q < QA + 2) {
+    const int j = q - QA;
+    __builtin_amdgcn_global_load_lds(b_src[j] + (int64_t)step * 32, (lds_void_t*)(d.b + 2048 * wave + 1024 * j), 16,
+                                     0, 0);
+  } else if constexpr (SCH == 2) {
     __builtin_amdgcn_global_load_lds(s_src + 4 * (step >> 1), (lds_void_t*)(d.s + 256 * wave), 4, 0, 0);
+  }
+}
+
+// All of one step's transfers of one wave.
+template <int QA, int SCH, class StageT>
+__device__ __forceinline__ void fwd_dma_issue(StageT& d, const uint8_t* const* a_src, const uint8_t* const* b_src,
+                                              const uint8_t* s_src, int wave, int step) {
+#pragma unroll
+  for (int q = 0; q < QA + 2 + (SCH == 2 ? 1 : 0); ++q) fwd_dma_op<QA, SCH>(d, a_src, b_src, s_src, wave, step, q);
 }
 
 // The 16-byte scale chunk c (steps 8c .. 8c+7) of this wave's 64 columns.
@@ -336,7 +342,13 @@ __device__ __forceinline__ void fwd_dma_scales8(DmaSmem<W, STAGES, 8>& sm, const
   __builtin_amdgcn_global_load_lds(s_src + 16 * chunk, (lds_void_t*)(sm.s8[chunk & 1] + 1024 * wave), 16, 0, 0);
 }
 
-template <int W, int STAGES, int MINWG, int SCH>
+// SPREAD: issue a step's transfers one or two at a time behind each
+// sub-step's fragment reads, so they go out between MFMAs instead of as one
+// burst ahead of them (a transfer cannot move past LDS reads of the ring on
+// its own: the compiler keeps LDS writes and reads in order).  Faster for
+// long reductions, slower for short ones (MI355X: +4% at K = 7168 and 4096,
+// -4% at K = 2048).
+template <int W, int STAGES, int MINWG, int SCH, bool SPREAD>
 __global__ void __launch_bounds__(W * 64, MINWG)
 k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
                      const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
@@ -410,7 +422,7 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
   if constexpr (SCH == 8) fwd_dma_scales8<W, STAGES>(sm, s_src, wave, 0);
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t)
-    fwd_dma_issue<W, STAGES, SCH>(sm.st[t], a_src, b_src, s_src, wave, min(t, last));
+    fwd_dma_issue<QA, SCH>(sm.st[t], a_src, b_src, s_src, wave, min(t, last));
   // step 0 (and scale chunk 0) have landed once only steps 1 .. STAGES-2 may be in flight
   wait_vmcnt_barrier<kOps * (STAGES - 2)>();
 
@@ -425,8 +437,9 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
       if (chunk_start) fwd_dma_scales8<W, STAGES>(sm, s_src, wave, min((s >> 3) + 1, last_chunk));
     }
     // refill the stage step s-1 used with step s + STAGES - 1
-    fwd_dma_issue<W, STAGES, SCH>(sm.st[stage == 0 ? STAGES - 1 : stage - 1], a_src, b_src, s_src, wave,
-                                  min(s + STAGES - 1, last));
+    typename Smem::Stage& nxt = sm.st[stage == 0 ? STAGES - 1 : stage - 1];
+    const int nstep = min(s + STAGES - 1, last);
+    if constexpr (!SPREAD) fwd_dma_issue<QA, SCH>(nxt, a_src, b_src, s_src, wave, nstep);
     const typename Smem::Stage& c = sm.st[stage];
     // decode this wave's weights for the step into B fragments
     bf16x8_t fb[NT][4];
@@ -455,6 +468,14 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
       bf16x8_t fa[MT];
 #pragma unroll
       for (int i = 0; i < MT; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(la + i * 32 * 128 + off);
+      if constexpr (SPREAD) {
+        // this sub-step's share of the next stage's transfers (same ops, same
+        // order, so the step-end vmcnt count is unchanged)
+        constexpr int kOpsAll = QA + 2 + (SCH == 2 ? 1 : 0);
+#pragma unroll
+        for (int q = kk * kOpsAll / 4; q < (kk + 1) * kOpsAll / 4; ++q)
+          fwd_dma_op<QA, SCH>(nxt, a_src, b_src, s_src, wave, nstep, q);
+      }
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -721,13 +742,20 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
       const int64_t gx8 = (wn_dim + 511) / 512;
       const bool wide = gx8 * gy >= 2 * 256;
       const dim3 g4((unsigned)gx, (unsigned)gy), g8((unsigned)gx8, (unsigned)gy);
-#define MXQ_FWD_LAUNCH(W, ST, WG, SCH, G)                                                                    \
-  hipLaunchKernelGGL((k_grouped_mm_fwd_dma<W, ST, WG, SCH>), G, dim3(W * 64), 0, st, (const uint8_t*)a,      \
+      const bool spread = wk_dim >= 4096;
+#define MXQ_FWD_LAUNCH(W, ST, WG, SCH, SP, G)                                                                \
+  hipLaunchKernelGGL((k_grouped_mm_fwd_dma<W, ST, WG, SCH, SP>), G, dim3(W * 64), 0, st, (const uint8_t*)a,  \
                      (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim, (uint8_t*)out)
-      if (wide && sch8) MXQ_FWD_LAUNCH(8, 3, 1, 8, g8);
-      else if (wide) MXQ_FWD_LAUNCH(8, 3, 1, 2, g8);
-      else if (sch8) MXQ_FWD_LAUNCH(4, 3, 2, 8, g4);
-      else MXQ_FWD_LAUNCH(4, 3, 2, 2, g4);
+#define MXQ_FWD_LAUNCH2(W, ST, WG, SCH, G)        \
+  do {                                            \
+    if (spread) MXQ_FWD_LAUNCH(W, ST, WG, SCH, true, G); \
+    else MXQ_FWD_LAUNCH(W, ST, WG, SCH, false, G);       \
+  } while (0)
+      if (wide && sch8) MXQ_FWD_LAUNCH2(8, 3, 1, 8, g8);
+      else if (wide) MXQ_FWD_LAUNCH2(8, 3, 1, 2, g8);
+      else if (sch8) MXQ_FWD_LAUNCH2(4, 3, 2, 8, g4);
+      else MXQ_FWD_LAUNCH2(4, 3, 2, 2, g4);
+#undef MXQ_FWD_LAUNCH2
 #undef MXQ_FWD_LAUNCH
       return hipGetLastError();
     }
