@@ -41,7 +41,7 @@ typedef enum {
   MXQ_ERR_DTYPE = -3,   /* dtype code not supported by this entry point        */
   MXQ_ERR_FORMAT = -4,  /* format code not one of mxq_format                   */
   MXQ_ERR_BLOCK = -5,   /* block_size <= 0                                     */
-  MXQ_ERR_ALIGN = -6,   /* (reserved)                                          */
+  MXQ_ERR_ALIGN = -6,   /* grouped GEMM activation / packed weights not 16-B aligned */
   MXQ_ERR_ALIAS = -7,   /* output overlaps an input that must stay unmodified  */
   MXQ_ERR_HIP = -8      /* a HIP launch reported an error                      */
 } mxq_status;
@@ -112,9 +112,13 @@ int quantize_cache_bwd(const void* grad_out, void* grad_in, int t, int64_t numel
  * W_e^T into y bf16 [tokens, n]: weights are dequantized on the fly (never
  * written to memory), products accumulate in fp32, output rounds nearest-even.
  * Rows at or past offs[experts-1] are written as zeros.
- * Preconditions not checked (they would need a device sync): offs is
- * non-decreasing and offs[experts-1] <= tokens.
- * Errors: MXQ_ERR_NULL, MXQ_ERR_SHAPE (k % 32 != 0, negative sizes).
+ * offs should be non-decreasing with offs[experts-1] <= tokens; this is not
+ * checked on the host (it would need a device sync).  The kernels clamp each
+ * offset into [clamped previous offset, tokens], so out-of-range offsets never
+ * cause an access past x or y; the result is then that of the clamped offsets.
+ * x and packed must be 16-byte aligned; y must not overlap x.
+ * Errors: MXQ_ERR_NULL, MXQ_ERR_SHAPE (negative sizes, k % 32 != 0 or
+ * n % 8 != 0), MXQ_ERR_ALIGN, MXQ_ERR_ALIAS, MXQ_ERR_HIP.
  */
 int mxfp4_grouped_mm_fwd(const void* x, int64_t tokens, int64_t k,
                          const int8_t* packed, const uint8_t* scales, int64_t experts, int64_t n,

@@ -56,7 +56,10 @@ __device__ __forceinline__ TileInfo find_tile(const int32_t* __restrict__ offs, 
   int64_t start = 0;
   int acc = 0;
   for (int e = 0; e < experts; ++e) {
-    const int64_t end = offs[e];
+    // offsets outside [previous, tokens] are clamped into it, so no tile ever
+    // reaches past the activation rows whatever offs holds
+    int64_t end = offs[e];
+    end = end < start ? start : (end > tokens ? tokens : end);
     const int tiles = (int)((end - start + BM - 1) / BM);
     if (slot < acc + tiles) return TileInfo{start + (int64_t)(slot - acc) * BM, end, e};
     acc += tiles;

@@ -102,6 +102,25 @@ def test_random_segments(E, T, N, K, counts):
     check_segments(bf16_values(gx), want_b, offs, what="bwd_x")
 
 
+@pytest.mark.parametrize("raw", [[300, 200, 900], [-5, 150, 40, 10_000]])
+def test_out_of_range_offsets_are_clamped(raw):
+    """Offsets that decrease, go negative or pass the row count are clamped
+    into [previous clamped offset, tokens] by the kernels: no access leaves
+    the buffers and the result is the oracle's on the clamped offsets."""
+    E, T, N, K = len(raw), 500, 256, 512
+    clamped = np.minimum(np.maximum.accumulate(np.maximum(np.array(raw), 0)), T).astype(np.int32)
+    packed, scales, xb = random_case(11 + E, E, T, N, K, clamped)
+    pt, st = gpu_weights(packed, scales)
+    ot = torch.tensor(raw, dtype=torch.int32, device=dev())
+    y = mxq.mxfp4_grouped_mm_fwd(to_gpu_bits(xb, "bf16"), pt, st, ot)
+    want = oracle.grouped_mm_fwd(oracle.from_dtype_bits(xb, "bf16"), packed, scales, clamped)
+    check_segments(bf16_values(y), want, clamped, what="fwd clamped offs")
+    gb = synth.normal_bf16(np.random.default_rng(E), (T, N), 0.1)
+    gx = mxq.mxfp4_grouped_mm_bwd_x(to_gpu_bits(gb, "bf16"), pt, st, ot)
+    want_b = oracle.grouped_mm_bwd_x(oracle.from_dtype_bits(gb, "bf16"), packed, scales, clamped)
+    check_segments(bf16_values(gx), want_b, clamped, what="bwd_x clamped offs")
+
+
 def test_autograd_function():
     E, T, N, K = 4, 400, 256, 512
     offs = np.array([100, 200, 300, 400], np.int32)
