@@ -130,7 +130,8 @@ int mxfp4_grouped_mm_fwd(const void* x, int64_t tokens, int64_t k,
  * grad_x[rows_e] = grad_out[rows_e] @ W_e into grad_x bf16 [tokens, k], with
  * a fresh on-the-fly dequantization; no weight gradient (frozen base).
  * Rows past offs[experts-1] are written as zeros.  Same preconditions and
- * errors as the forward.
+ * errors as the forward; also MXQ_ERR_SHAPE when n > 2^22 or one expert's
+ * packed weights reach 2 GiB (n * k / 2 >= 2^31).
  */
 int mxfp4_grouped_mm_bwd_x(const void* grad_out, int64_t tokens, int64_t n,
                            const int8_t* packed, const uint8_t* scales, int64_t experts, int64_t k,

@@ -94,6 +94,8 @@ int mxfp4_grouped_mm_bwd_x(const void* grad_out, int64_t tokens, int64_t n, cons
                            void* stream) {
   const int st = grouped_mm_check(grad_out, tokens, n, packed, scales, experts, k, offs, grad_x, k, n);
   if (st != MXQ_OK) return st;
+  // the kernel addresses a row tile of grad_out and one expert's weights with 32-bit offsets
+  if (n > (int64_t(1) << 22) || n * (k / 2) >= (int64_t(1) << 31)) return MXQ_ERR_SHAPE;
   if (tokens == 0 || k == 0) return MXQ_OK;
   if (n == 0 || experts == 0) {
     return from_hip(mxq::launch_zero(grad_x, tokens * k * 2, (hipStream_t)stream));

@@ -520,38 +520,53 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
 // ----------------------------------------------------------------- backward
 // grad_x = grad_out @ W_e.  Tile: 128 token rows x 256 output columns (k),
 // reduction over n in steps of 64; 4 waves split the columns (wave tile
-// 128 x 64), two workgroups per CU.  All global loads go to registers one
-// step ahead (addresses clamped into range, out-of-range values replaced by
-// zeros), so the compiler's in-order vmcnt accounting stays exact.
-//  * grad_out tile (128 x 64 bf16) is staged through registers into a
-//    double-buffered LDS tile (same (row >> 1) & 7 chunk swizzle as the
-//    DMA forward);
-//  * weights: lane l of a wave fetches the 32 packed bytes (64 values) of
-//    weight row n0 + l in the wave's 64 columns and their two scale bytes,
-//    decodes them along k -- the direction the scaled fp4 conversion and
-//    the E8M0 block both run -- and writes the bf16 row, in 16-byte chunks,
-//    into a wave-private tile Wd[n][k] (no barrier needed);
+// 128 x 64), two workgroups per CU.  Global loads are raw buffer loads over
+// the tile's valid range: the hardware returns zeros past it, so rows past
+// the expert's end, n past the weight rows and column halves past k need no
+// masking (an out-of-range chunk gets an offset past every range).
+//  * grad_out tile (128 x 64 bf16) is loaded into registers one step ahead
+//    and stored into a double-buffered LDS tile (same (row >> 1) & 7 chunk
+//    swizzle as the DMA forward);
+//  * weights: each step's 64 x 64 block of the wave's columns is fetched two
+//    steps ahead as 64 pieces of 16 packed bytes (32 values of one row) and
+//    one scale byte, one per lane, decoded along k -- the direction the
+//    scaled fp4 conversion and the E8M0 block both run -- and written, in
+//    16-byte chunks, into a wave-private tile Wd[n][k] (no barrier needed);
 //  * the B fragments, which need 8 consecutive n of one column per lane,
 //    come out of Wd with gfx950's transposing LDS read ds_read_b64_tr_b16:
 //    within each group of 16 lanes, output lane i, element e is element
 //    i % 4 of source lane 4e + i / 4, so source lanes pointing at
 //    Wd[n0 + s/4][c0 + 4(s%4)] (s = lane % 16) hand lane i the four values
 //    Wd[n0 .. n0+3][c0 + i]; two reads give the 8 values of a fragment;
-//  * Wd's 16-byte chunk c of row n is stored at chunk c ^ swz(n), swz(n) =
-//    ((m & 1) << 2) | (m >> 1) with m = (n >> 1) & 7: the row-wise writes
-//    (16 rows, one chunk) and the transposing reads (4 rows, one aligned
-//    quad of chunks) both hit distinct 16-byte bank groups;
 //  * MFMA fragments as in the forward: lane-half h covers n in
-//    [32h, 32h + 32) of the step, sub-step kk the 8 values 32h + 8kk ..
+//    [32h, 32h + 32) of the step, sub-step kk the 8 values 32h + 8kk ..,
+//    so sub-steps 0-1 read Wd rows {0..15, 32..47} and 2-3 the other 32.
+//    Lane l's first piece is a row of the first set and its second a row
+//    of the second set, which lets the next step's decode run between this
+//    step's MFMAs and its writes follow the last reads of each row set;
+//  * Wd's 16-byte chunk c of row n sits at chunk c ^ swz(n), swz(n) =
+//    4 * ((n >> 1) & 1) + ((n >> 1) & 3): the piece writes (8 consecutive
+//    rows, both column halves, one chunk each) and the transposing reads
+//    (4 consecutive rows, one aligned quad of chunks) hit distinct 16-byte
+//    groups of the 64 LDS banks.
 constexpr int kBwdBM = 128, kBwdBN = 256;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-__device__ __forceinline__ int wd_swz(int n) {
-  const int m = (n >> 1) & 7;
-  return ((m & 1) << 2) | (m >> 1);
+__device__ __forceinline__ int wd_swz(int n) { return (((n >> 1) & 1) << 2) | ((n >> 1) & 3); }
+
+// raw buffer over [base, base + bytes) (bytes < 2^31): loads at offsets past
+// the range return zeros
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+constexpr uint32_t kBufOob = 0x80000000u;   // offset past every range used here
+
+struct WRaw {          // one step's weight pieces of a lane (2 x 16 packed bytes + 2 scale bytes)
+  u32x4_t pk[2];
+  uint32_t sb[2];
+};
 
 __global__ void __launch_bounds__(kGemmThreads, 2)
 k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ packed,
@@ -580,78 +595,59 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
   __shared__ __attribute__((aligned(1024))) uint8_t lds_g[2][BM * 128];
   __shared__ __attribute__((aligned(1024))) uint8_t lds_w[4][64 * 128];
 
-  // grad_out staging: thread t owns chunks c = t + 256 i: row c / 8, chunk c % 8
-  const uint8_t* g_row[GC];                            // start of the (clamped) row
-#pragma unroll
-  for (int i = 0; i < GC; ++i) {
-    const int c = threadIdx.x + i * kThreads;
-    int64_t row = ti.row0 + (c >> 3);
-    if (row >= ti.row_end) row = ti.row_end - 1;       // never stored
-    g_row[i] = g + row * ndim * 2;
-  }
-  const int g_col = (threadIdx.x & 7) * 8;             // same chunk for all i
-  // Loads are unconditional (clamped addresses) and their values are masked
-  // only where they are consumed: a select next to a load becomes a branch
-  // around it, and a mask next to it inside a conditional block makes the
-  // compiler wait for the load right there.
+  // grad_out: thread t owns chunks c = t + 256 i: tile row c / 8 = t / 8 + 32 i, chunk t % 8
+  const __amdgpu_buffer_rsrc_t rs_g = buf_rsrc(g + ti.row0 * ndim * 2, (ti.row_end - ti.row0) * ndim * 2);
+  const int g_col = (threadIdx.x & 7) * 8;
+  const uint32_t g_off0 = (uint32_t)((threadIdx.x >> 3) * ndim + g_col) * 2;
+  const uint32_t g_row_step = (uint32_t)(32 * ndim * 2);
   u32x4_t gr_regs[GC];
-  uint32_t g_mask = 0;
   auto load_g = [&](int64_t n0) {
-    // n tail: chunks are 8-aligned and N % 8 == 0, so a chunk is wholly in or out;
-    // an out-of-range chunk reads the row's first chunk and is zeroed
-    const bool ok = n0 + g_col < ndim;
-    const int64_t off = ok ? (n0 + g_col) * 2 : 0;
-    g_mask = ok ? ~0u : 0u;
+    // N % 8 == 0: a chunk is wholly in or out of range
+    const uint32_t base = n0 + g_col < ndim ? g_off0 + (uint32_t)(n0 * 2) : kBufOob;
 #pragma unroll
-    for (int i = 0; i < GC; ++i) gr_regs[i] = *reinterpret_cast<const u32x4_t*>(g_row[i] + off);
+    for (int i = 0; i < GC; ++i)
+      gr_regs[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rs_g, base == kBufOob ? kBufOob : base + i * g_row_step, 0, 0));
   };
   auto store_g = [&](uint8_t* dst) {
 #pragma unroll
     for (int i = 0; i < GC; ++i) {
       const int c = threadIdx.x + i * kThreads;
       const int row = c >> 3, chunk = c & 7;
-      *reinterpret_cast<u32x4_t*>(dst + row * 128 + 16 * (chunk ^ ((row >> 1) & 7))) = gr_regs[i] & g_mask;
+      *reinterpret_cast<u32x4_t*>(dst + row * 128 + 16 * (chunk ^ ((row >> 1) & 7))) = gr_regs[i];
     }
   };
 
-  // weights: lane l takes row n0 + l, columns kc .. kc + 63 (two 16-byte halves)
+  // weights: piece p of lane l is row wrow[p] of the step's 64, column half l & 1 of the wave's 64 columns
+  const int wj = lane >> 1, whalf = lane & 1;
+  const int wrow[2] = {(wj & 15) + 32 * (wj >> 4), 16 + (wj & 15) + 32 * (wj >> 4)};
   const int64_t kc = col0 + wave * 64;
-  const bool v0 = kc + 32 <= kdim, v1 = kc + 64 <= kdim;   // K % 32 == 0: halves are all in or all out
-  const int64_t prow = kdim / 2, srow = kdim / 32;           // bytes per weight row (packed, scales)
-  const uint8_t* pe = packed_e_of(packed, ti.expert, ndim, kdim);
-  const uint8_t* se = scales + (int64_t)ti.expert * ndim * srow;
-  const int64_t off0 = v0 ? kc / 2 : 0, off1 = v1 ? kc / 2 + 16 : 0;
-  const int64_t soff0 = v0 ? kc / 32 : 0, soff1 = v1 ? kc / 32 + 1 : 0;
-  u32x4_t raw[2];
-  uint32_t sb[2], wm[2];
-  auto load_w = [&](int64_t n0) {
-    const int64_t n = n0 + lane;
-    const bool ok = n < ndim;
-    const int64_t nn = ok ? n : ndim - 1;
-    raw[0] = *reinterpret_cast<const u32x4_t*>(pe + nn * prow + off0);
-    raw[1] = *reinterpret_cast<const u32x4_t*>(pe + nn * prow + off1);
-    sb[0] = se[nn * srow + soff0];
-    sb[1] = se[nn * srow + soff1];
-    // rows / columns out of range decode to zeros (code 0, scale byte 127)
-    wm[0] = ok && v0 ? ~0u : 0u;
-    wm[1] = ok && v1 ? ~0u : 0u;
+  const bool wvalid = kc + 32 * (whalf + 1) <= kdim;             // K % 32 == 0: halves all in or all out
+  const int64_t prow = kdim / 2, srow = kdim / 32;               // bytes per weight row (packed, scales)
+  const __amdgpu_buffer_rsrc_t rs_w = buf_rsrc(packed_e_of(packed, ti.expert, ndim, kdim), ndim * prow);
+  const __amdgpu_buffer_rsrc_t rs_s = buf_rsrc(scales + (int64_t)ti.expert * ndim * srow, ndim * srow);
+  const uint32_t wcol = (uint32_t)(kc / 2 + 16 * whalf), scol = (uint32_t)(kc / 32 + whalf);
+  auto load_w = [&](WRaw& w, int64_t n0) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int64_t n = n0 + wrow[p];
+      const bool ok = wvalid && n < ndim;
+      w.pk[p] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rs_w, ok ? (uint32_t)(n * prow) + wcol : kBufOob, 0, 0));
+      w.sb[p] = __builtin_amdgcn_raw_buffer_load_b8(rs_s, ok ? (uint32_t)(n * srow) + scol : kBufOob, 0, 0);
+    }
   };
   uint8_t* wd = lds_w[wave];
-  auto build_wd = [&]() {
-    const int swz = wd_swz(lane);
+  // decode piece p (32 values) and write it into Wd, 16 bytes at a time
+  auto put_piece = [&](const WRaw& w, int p) {
+    const float sc = e8m0_to_f32(w.sb[p]);
+    const uint32_t w4[4] = {w.pk[p].x, w.pk[p].y, w.pk[p].z, w.pk[p].w};
+    const int row = wrow[p], swz = wd_swz(row);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const float sc = e8m0_to_f32((sb[half] & wm[half]) | (127u & ~wm[half]));
-      const u32x4_t p = raw[half] & wm[half];
-      const uint32_t w4[4] = {p.x, p.y, p.z, p.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const u32x4_t v = {dec_fp4_bf16x2<0>(w4[q], sc), dec_fp4_bf16x2<1>(w4[q], sc), dec_fp4_bf16x2<2>(w4[q], sc),
-                           dec_fp4_bf16x2<3>(w4[q], sc)};
-        const int chunk = 4 * half + q;   // columns 8 chunk .. 8 chunk + 7
-        *reinterpret_cast<u32x4_t*>(wd + lane * 128 + 16 * (chunk ^ swz)) = v;
-      }
-    }
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<u32x4_t*>(wd + row * 128 + 16 * ((4 * whalf + q) ^ swz)) =
+          u32x4_t{dec_fp4_bf16x2<0>(w4[q], sc), dec_fp4_bf16x2<1>(w4[q], sc), dec_fp4_bf16x2<2>(w4[q], sc),
+                  dec_fp4_bf16x2<3>(w4[q], sc)};
   };
   // transposing-read addresses: group gq = lane / 16 -> h = gq / 2, column
   // half gq % 2; source lane s = lane % 16 -> row a = s / 4, columns 4 (s % 4)
@@ -665,51 +661,64 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x16_t{};
 
-  const int nsteps = (int)((ndim + kBK - 1) / kBK);
-  load_g(0);
-  load_w(0);
-  store_g(lds_g[0]);
-  __syncthreads();
-
   const int swz_g = (r >> 1) & 7;
-  for (int s = 0; s < nsteps; ++s) {
-    const int cur = s & 1;
-    build_wd();                                   // this step's weights -> this wave's Wd
-    // the next step's loads (clamped at the end: in range, never used)
-    load_g((int64_t)min(s + 1, nsteps - 1) * kBK);
-    load_w((int64_t)min(s + 1, nsteps - 1) * kBK);
-    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the MFMAs
-    const uint8_t* la = lds_g[cur] + r * 128;
+  auto substep = [&](const uint8_t* la, int kk) {
+    const int off = 16 * ((4 * h + kk) ^ swz_g);
+    bf16x8_t fa[MT], fb[NT];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int off = 16 * ((4 * h + kk) ^ swz_g);
-      bf16x8_t fa[MT], fb[NT];
+    for (int i = 0; i < MT; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(la + i * 32 * 128 + off);
 #pragma unroll
-      for (int i = 0; i < MT; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(la + i * 32 * 128 + off);
+    for (int j = 0; j < NT; ++j) {
+      const int col = tr_col + 32 * j;
+      v4i16_t t[2];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        const int col = tr_col + 32 * j;
-        v4i16_t t[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int n = tr_row + 8 * kk + 4 * u;
-          const uint8_t* src = wd + n * 128 + 16 * ((col >> 3) ^ wd_swz(n)) + 2 * (col & 7);
-          t[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(src));
-        }
-        fb[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int u = 0; u < 2; ++u) {
+        const int n = tr_row + 8 * kk + 4 * u;
+        const uint8_t* src = wd + n * 128 + 16 * ((col >> 3) ^ wd_swz(n)) + 2 * (col & 7);
+        t[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(src));
       }
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      fb[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
     }
-    // unconditional (the last step stores a clamped copy nobody reads): a
-    // conditional store would let the compiler sink the loads into its block;
-    // the barrier keeps the masking of the loaded values after the MFMAs
-    __builtin_amdgcn_sched_barrier(0);
-    store_g(lds_g[cur ^ 1]);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+  };
+
+  const int nsteps = (int)((ndim + kBK - 1) / kBK);
+  WRaw w0, w1;
+  {
+    load_w(w1, 0);
+    load_w(w0, kBK);
+    load_g(0);
+    put_piece(w1, 0);
+    put_piece(w1, 1);
+    store_g(lds_g[0]);
     __syncthreads();
+  }
+  // step s: MFMAs on Wd(s) and the grad_out tile in lds_g[s & 1]; `cur` holds
+  // the raw weights of step s + 1 (decoded into Wd behind this step's reads),
+  // `nxt` receives those of step s + 2; grad_out of step s + 1 goes through
+  // registers into the other LDS tile.  Loads past the last step read zeros.
+  auto step = [&](WRaw& cur, WRaw& nxt, int s) {
+    load_g((int64_t)(s + 1) * kBK);
+    load_w(nxt, (int64_t)(s + 2) * kBK);
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the MFMAs
+    const uint8_t* la = lds_g[s & 1] + r * 128;
+    substep(la, 0);
+    substep(la, 1);
+    put_piece(cur, 0);                   // rows of sub-steps 0-1: read above
+    substep(la, 2);
+    substep(la, 3);
+    put_piece(cur, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_g(lds_g[(s & 1) ^ 1]);
+    __syncthreads();
+  };
+  for (int s = 0; s < nsteps; s += 2) {
+    step(w0, w1, s);
+    if (s + 1 < nsteps) step(w1, w0, s + 1);
   }
 
 #pragma unroll

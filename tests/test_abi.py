@@ -93,6 +93,9 @@ def test_grouped_mm_validation(L):
     b = L.mxfp4_grouped_mm_bwd_x
     assert b(FAKE, 16, 64, FAKE * 2, FAKE * 3, 2, 40, FAKE * 4, FAKE * 5, None) == -2    # k % 32
     assert b(FAKE, 16, 64, FAKE * 2, FAKE * 3, -1, 64, FAKE * 4, FAKE * 5, None) == -2
+    # 32-bit addressing limits of the backward: n <= 2^22 and n * k / 2 < 2^31
+    assert b(FAKE, 1, (1 << 22) + 8, FAKE * 2, FAKE * 3, 2, 64, FAKE * 4, FAKE << 12, None) == -2
+    assert b(FAKE, 1, 1 << 16, FAKE * 2, FAKE * 3, 2, 1 << 16, FAKE * 4, FAKE * 5, None) == -2
 
 
 def test_ops_reject_cpu_tensors():
