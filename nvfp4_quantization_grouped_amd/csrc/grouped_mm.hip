@@ -518,20 +518,26 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
 }
 
 // ----------------------------------------------------------------- backward
-// grad_x = grad_out @ W_e.  Tile: 128 token rows x 256 output columns (k),
-// reduction over n in steps of 64; 4 waves split the columns (wave tile
-// 128 x 64), two workgroups per CU.  Global loads are raw buffer loads over
-// the tile's valid range: the hardware returns zeros past it, so rows past
-// the expert's end, n past the weight rows and column halves past k need no
-// masking (an out-of-range chunk gets an offset past every range).
-//  * grad_out tile (128 x 64 bf16) is loaded into registers one step ahead
+// grad_x = grad_out @ W_e.  Tile: 256 token rows x 256 output columns (k),
+// reduction over n in steps of 64; 8 waves, one workgroup per CU.  Wave
+// (wm, wn) = (wave / 4, wave % 4) owns rows [128 wm, 128 wm + 128) and
+// columns [64 wn, 64 wn + 64) of the tile (4 x 2 MFMA tiles), so the two
+// waves of a column block share its decoded weights: each step's 64 x 256
+// weight block is decoded once for 256 rows.  Global loads are raw buffer
+// loads over the tile's valid range: the hardware returns zeros past it, so
+// rows past the expert's end, n past the weight rows and column halves past
+// k need no masking (an out-of-range chunk gets an offset past every range).
+//  * grad_out tile (256 x 64 bf16) is loaded into registers one step ahead
 //    and stored into a double-buffered LDS tile (same (row >> 1) & 7 chunk
 //    swizzle as the DMA forward);
-//  * weights: each step's 64 x 64 block of the wave's columns is fetched two
-//    steps ahead as 64 pieces of 16 packed bytes (32 values of one row) and
-//    one scale byte, one per lane, decoded along k -- the direction the
-//    scaled fp4 conversion and the E8M0 block both run -- and written, in
-//    16-byte chunks, into a wave-private tile Wd[n][k] (no barrier needed);
+//  * weights: wave (wm, wn) fetches, two steps ahead, rows [32 wm, 32 wm +
+//    32) of the step's 64 in its 64 columns -- one piece of 16 packed bytes
+//    (32 values of one row) and its scale byte per lane -- decodes it along
+//    k (the direction the scaled fp4 conversion and the E8M0 block both run)
+//    once the previous step's MFMAs are issued, so the conversions overlap
+//    their execution, and writes it in 16-byte chunks into the column
+//    block's tile Wd[n][k] of the next step (double-buffered, so the barrier
+//    that ends the step publishes it);
 //  * the B fragments, which need 8 consecutive n of one column per lane,
 //    come out of Wd with gfx950's transposing LDS read ds_read_b64_tr_b16:
 //    within each group of 16 lanes, output lane i, element e is element
@@ -539,17 +545,13 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
 //    Wd[n0 + s/4][c0 + 4(s%4)] (s = lane % 16) hand lane i the four values
 //    Wd[n0 .. n0+3][c0 + i]; two reads give the 8 values of a fragment;
 //  * MFMA fragments as in the forward: lane-half h covers n in
-//    [32h, 32h + 32) of the step, sub-step kk the 8 values 32h + 8kk ..,
-//    so sub-steps 0-1 read Wd rows {0..15, 32..47} and 2-3 the other 32.
-//    Lane l's first piece is a row of the first set and its second a row
-//    of the second set, which lets the next step's decode run between this
-//    step's MFMAs and its writes follow the last reads of each row set;
+//    [32h, 32h + 32) of the step, sub-step kk the 8 values 32h + 8kk ..;
 //  * Wd's 16-byte chunk c of row n sits at chunk c ^ swz(n), swz(n) =
 //    4 * ((n >> 1) & 1) + ((n >> 1) & 3): the piece writes (8 consecutive
 //    rows, both column halves, one chunk each) and the transposing reads
 //    (4 consecutive rows, one aligned quad of chunks) hit distinct 16-byte
 //    groups of the 64 LDS banks.
-constexpr int kBwdBM = 128, kBwdBN = 256;
+constexpr int kBwdBM = 256, kBwdBN = 256, kBwdThreads = 512;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
@@ -563,21 +565,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int
 }
 constexpr uint32_t kBufOob = 0x80000000u;   // offset past every range used here
 
-struct WRaw {          // one step's weight pieces of a lane (2 x 16 packed bytes + 2 scale bytes)
-  u32x4_t pk[2];
-  uint32_t sb[2];
+struct WRaw {          // one step's weight piece of a lane (16 packed bytes + scale byte)
+  u32x4_t pk;
+  uint32_t sb;
 };
 
-__global__ void __launch_bounds__(kGemmThreads, 2)
+struct BwdSmem {
+  uint8_t g[2][kBwdBM * 128];                // grad_out tiles, 256 rows x 128 bytes
+  uint8_t w[2][4][64 * 128];                 // decoded weights per column block, 64 n x 64 k bf16
+};
+
+__global__ void __launch_bounds__(kBwdThreads, 1)
 k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ packed,
                  const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
                  int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out) {
-  constexpr int BM = kBwdBM, BN = kBwdBN, MT = BM / 32, NT = 2, kThreads = kGemmThreads;
+  constexpr int BM = kBwdBM, BN = kBwdBN, MT = 4, NT = 2, kThreads = kBwdThreads;
   constexpr int GC = BM * 8 / kThreads;                // 16-byte grad_out chunks per thread and step
   const int64_t col0 = (int64_t)blockIdx.x * BN;
   const TileInfo ti = find_tile<BM>(offs, experts, tokens, blockIdx.y);
   if (ti.expert == -2) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
   const int h = lane >> 5, r = lane & 31;
 
   if (ti.expert == -1) {
@@ -592,68 +600,71 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
     return;
   }
 
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_g[2][BM * 128];
-  __shared__ __attribute__((aligned(1024))) uint8_t lds_w[4][64 * 128];
+  __shared__ __attribute__((aligned(1024))) BwdSmem sm;
 
-  // grad_out: thread t owns chunks c = t + 256 i: tile row c / 8 = t / 8 + 32 i, chunk t % 8
+  // grad_out: thread t owns chunks c = t + 512 i: tile row c / 8 = t / 8 + 64 i, chunk t % 8
   const __amdgpu_buffer_rsrc_t rs_g = buf_rsrc(g + ti.row0 * ndim * 2, (ti.row_end - ti.row0) * ndim * 2);
   const int g_col = (threadIdx.x & 7) * 8;
   const uint32_t g_off0 = (uint32_t)((threadIdx.x >> 3) * ndim + g_col) * 2;
-  const uint32_t g_row_step = (uint32_t)(32 * ndim * 2);
+  const uint32_t g_row_step = (uint32_t)(64 * ndim * 2);
   u32x4_t gr_regs[GC];
   auto load_g = [&](int64_t n0) {
     // N % 8 == 0: a chunk is wholly in or out of range
-    const uint32_t base = n0 + g_col < ndim ? g_off0 + (uint32_t)(n0 * 2) : kBufOob;
+    const bool ok = n0 + g_col < ndim;
+    const uint32_t base = g_off0 + (uint32_t)(n0 * 2);
 #pragma unroll
     for (int i = 0; i < GC; ++i)
       gr_regs[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   rs_g, base == kBufOob ? kBufOob : base + i * g_row_step, 0, 0));
+                                                   rs_g, ok ? base + i * g_row_step : kBufOob, 0, 0));
   };
+  // (row >> 1) & 7 of the rows t / 8 + 64 i does not depend on i
+  const int g_st = (threadIdx.x >> 3) * 128 + 16 * ((threadIdx.x & 7) ^ ((threadIdx.x >> 4) & 7));
   auto store_g = [&](uint8_t* dst) {
 #pragma unroll
-    for (int i = 0; i < GC; ++i) {
-      const int c = threadIdx.x + i * kThreads;
-      const int row = c >> 3, chunk = c & 7;
-      *reinterpret_cast<u32x4_t*>(dst + row * 128 + 16 * (chunk ^ ((row >> 1) & 7))) = gr_regs[i];
-    }
+    for (int i = 0; i < GC; ++i) *reinterpret_cast<u32x4_t*>(dst + g_st + i * 64 * 128) = gr_regs[i];
   };
 
-  // weights: piece p of lane l is row wrow[p] of the step's 64, column half l & 1 of the wave's 64 columns
-  const int wj = lane >> 1, whalf = lane & 1;
-  const int wrow[2] = {(wj & 15) + 32 * (wj >> 4), 16 + (wj & 15) + 32 * (wj >> 4)};
-  const int64_t kc = col0 + wave * 64;
+  // weights: lane l of wave (wm, wn) takes row 32 wm + l / 2 of the step, column half l & 1
+  const int wrow = 32 * wm + (lane >> 1), whalf = lane & 1;
+  const int64_t kc = col0 + wn * 64;
   const bool wvalid = kc + 32 * (whalf + 1) <= kdim;             // K % 32 == 0: halves all in or all out
   const int64_t prow = kdim / 2, srow = kdim / 32;               // bytes per weight row (packed, scales)
   const __amdgpu_buffer_rsrc_t rs_w = buf_rsrc(packed_e_of(packed, ti.expert, ndim, kdim), ndim * prow);
   const __amdgpu_buffer_rsrc_t rs_s = buf_rsrc(scales + (int64_t)ti.expert * ndim * srow, ndim * srow);
   const uint32_t wcol = (uint32_t)(kc / 2 + 16 * whalf), scol = (uint32_t)(kc / 32 + whalf);
   auto load_w = [&](WRaw& w, int64_t n0) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int64_t n = n0 + wrow[p];
-      const bool ok = wvalid && n < ndim;
-      w.pk[p] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rs_w, ok ? (uint32_t)(n * prow) + wcol : kBufOob, 0, 0));
-      w.sb[p] = __builtin_amdgcn_raw_buffer_load_b8(rs_s, ok ? (uint32_t)(n * srow) + scol : kBufOob, 0, 0);
-    }
+    const int64_t n = n0 + wrow;
+    const bool ok = wvalid && n < ndim;
+    w.pk = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs_w, ok ? (uint32_t)(n * prow) + wcol : kBufOob, 0, 0));
+    w.sb = __builtin_amdgcn_raw_buffer_load_b8(rs_s, ok ? (uint32_t)(n * srow) + scol : kBufOob, 0, 0);
   };
-  uint8_t* wd = lds_w[wave];
-  // decode piece p (32 values) and write it into Wd, 16 bytes at a time
-  auto put_piece = [&](const WRaw& w, int p) {
-    const float sc = e8m0_to_f32(w.sb[p]);
-    const uint32_t w4[4] = {w.pk[p].x, w.pk[p].y, w.pk[p].z, w.pk[p].w};
-    const int row = wrow[p], swz = wd_swz(row);
+  const int wd_st = wrow * 128, wd_swz_row = wd_swz(wrow);
+  // decode a piece (32 values) and write it into Wd, 16 bytes at a time
+  auto put_piece = [&](const WRaw& w, uint8_t* wd) {
+    const float sc = e8m0_to_f32(w.sb);
+    const uint32_t w4[4] = {w.pk.x, w.pk.y, w.pk.z, w.pk.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<u32x4_t*>(wd + row * 128 + 16 * ((4 * whalf + q) ^ swz)) =
+      *reinterpret_cast<u32x4_t*>(wd + wd_st + 16 * ((4 * whalf + q) ^ wd_swz_row)) =
           u32x4_t{dec_fp4_bf16x2<0>(w4[q], sc), dec_fp4_bf16x2<1>(w4[q], sc), dec_fp4_bf16x2<2>(w4[q], sc),
                   dec_fp4_bf16x2<3>(w4[q], sc)};
   };
   // transposing-read addresses: group gq = lane / 16 -> h = gq / 2, column
-  // half gq % 2; source lane s = lane % 16 -> row a = s / 4, columns 4 (s % 4)
+  // half gq % 2; source lane s = lane % 16 -> row a = s / 4, columns 4 (s % 4).
+  // Rows tr_row + 8 kk + 4 u: the swizzle depends on u only, so sub-step kk
+  // is the immediate offset 1024 kk.
   const int gq = lane >> 4, sl = lane & 15;
-  const int tr_row = 32 * (gq >> 1) + (sl >> 2);          // + 8 kk (+ 4)
-  const int tr_col = 16 * (gq & 1) + 4 * (sl & 3);        // + 32 j
+  const int tr_row = 32 * (gq >> 1) + (sl >> 2);
+  const int tr_col = 16 * (gq & 1) + 4 * (sl & 3);
+  int tr_off[2][NT];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int n = tr_row + 4 * u, col = tr_col + 32 * j;
+      tr_off[u][j] = n * 128 + 16 * ((col >> 3) ^ wd_swz(n)) + 2 * (col & 7);
+    }
 
   f32x16_t acc[MT][NT];
 #pragma unroll
@@ -662,58 +673,63 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x16_t{};
 
   const int swz_g = (r >> 1) & 7;
-  auto substep = [&](const uint8_t* la, int kk) {
+  struct Frags { bf16x8_t fa[MT], fb[NT]; };
+  auto read_frags = [&](Frags& f, const uint8_t* la, const uint8_t* wd, int kk) {
     const int off = 16 * ((4 * h + kk) ^ swz_g);
-    bf16x8_t fa[MT], fb[NT];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(la + i * 32 * 128 + off);
+    for (int i = 0; i < MT; ++i) f.fa[i] = *reinterpret_cast<const bf16x8_t*>(la + i * 32 * 128 + off);
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int col = tr_col + 32 * j;
       v4i16_t t[2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int n = tr_row + 8 * kk + 4 * u;
-        const uint8_t* src = wd + n * 128 + 16 * ((col >> 3) ^ wd_swz(n)) + 2 * (col & 7);
-        t[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(src));
-      }
-      fb[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int u = 0; u < 2; ++u)
+        t[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(wd + tr_off[u][j] + 1024 * kk));
+      f.fb[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
     }
+  };
+  auto mfmas = [&](const Frags& f) {
 #pragma unroll
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int j = 0; j < NT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.fa[i], f.fb[j], acc[i][j], 0, 0, 0);
   };
 
   const int nsteps = (int)((ndim + kBK - 1) / kBK);
   WRaw w0, w1;
-  {
-    load_w(w1, 0);
-    load_w(w0, kBK);
-    load_g(0);
-    put_piece(w1, 0);
-    put_piece(w1, 1);
-    store_g(lds_g[0]);
-    __syncthreads();
-  }
-  // step s: MFMAs on Wd(s) and the grad_out tile in lds_g[s & 1]; `cur` holds
-  // the raw weights of step s + 1 (decoded into Wd behind this step's reads),
-  // `nxt` receives those of step s + 2; grad_out of step s + 1 goes through
-  // registers into the other LDS tile.  Loads past the last step read zeros.
+  load_w(w1, 0);
+  load_w(w0, kBK);
+  load_g(0);
+  put_piece(w1, sm.w[0][wn]);
+  store_g(sm.g[0]);
+  __syncthreads();
+  // step s: MFMAs on the grad_out tile and Wd of buffer s & 1, with each
+  // sub-step's fragments read one sub-step ahead.  All waves reach the LDS
+  // at once after the barrier, so the first fragment reads go out before
+  // the next step's global loads: grad_out of step s + 1 (through registers
+  // into the other tile at the end of the step) and the raw weights of step
+  // s + 2 (into `nxt`).  `cur` holds the raw weights of step s + 1, fetched
+  // a step earlier and decoded into the other Wd buffer behind the MFMAs.
+  // Loads past the last step read zeros.
   auto step = [&](WRaw& cur, WRaw& nxt, int s) {
-    load_g((int64_t)(s + 1) * kBK);
-    load_w(nxt, (int64_t)(s + 2) * kBK);
-    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the MFMAs
-    const uint8_t* la = lds_g[s & 1] + r * 128;
-    substep(la, 0);
-    substep(la, 1);
-    put_piece(cur, 0);                   // rows of sub-steps 0-1: read above
-    substep(la, 2);
-    substep(la, 3);
-    put_piece(cur, 1);
+    const uint8_t* la = sm.g[s & 1] + (128 * wm + r) * 128;
+    const uint8_t* wd = sm.w[s & 1][wn];
+    Frags f[2];
+    read_frags(f[0], la, wd, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk < 3) read_frags(f[(kk + 1) & 1], la, wd, kk + 1);
+      mfmas(f[kk & 1]);
+      if (kk == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_g((int64_t)(s + 1) * kBK);
+        load_w(nxt, (int64_t)(s + 2) * kBK);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    put_piece(cur, sm.w[(s & 1) ^ 1][wn]);
     __builtin_amdgcn_sched_barrier(0);
-    store_g(lds_g[(s & 1) ^ 1]);
+    store_g(sm.g[(s & 1) ^ 1]);
     __syncthreads();
   };
   for (int s = 0; s < nsteps; s += 2) {
@@ -725,10 +741,10 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
   for (int i = 0; i < MT; ++i) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      const int64_t gc = col0 + wave * 64 + j * 32 + r;
+      const int64_t gc = col0 + wn * 64 + j * 32 + r;
 #pragma unroll
       for (int q = 0; q < 16; q += 2) {
-        const int64_t gr0 = ti.row0 + i * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
+        const int64_t gr0 = ti.row0 + 128 * wm + i * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
         f32x2_t v = {acc[i][j][q], acc[i][j][q + 1]};
         const uint32_t bb = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
         if (gc < kdim) {
@@ -779,7 +795,7 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
   {
     const int64_t gx = (wk_dim + kBwdBN - 1) / kBwdBN;
     const int64_t gy = (tokens + kBwdBM - 1) / kBwdBM + experts;
-    hipLaunchKernelGGL(k_grouped_mm_bwd, dim3((unsigned)gx, (unsigned)gy), dim3(kGemmThreads), 0, st,
+    hipLaunchKernelGGL(k_grouped_mm_bwd, dim3((unsigned)gx, (unsigned)gy), dim3(kBwdThreads), 0, st,
                        (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim,
                        (uint8_t*)out);
     return hipGetLastError();
