@@ -10,10 +10,11 @@
 //
 // Every wave owns a 128-row x 64-column output tile (4 x 2 MFMA tiles, 128
 // fp32 accumulators per lane) and runs two to a SIMD, so one's memory phase
-// overlaps the other's MFMAs.  Workgroups of 4 waves (128 x 256 tiles, two
-// per CU) serve every shape; large forwards use workgroups of 8 waves
-// (128 x 512 tiles, one per CU), which move half the activation bytes per
-// output element.  The reduction runs in steps of
+// overlaps the other's MFMAs.  Forward workgroups of 4 waves (128 x 256
+// tiles, two per CU) serve every shape; large forwards use workgroups of 8
+// waves (128 x 512 tiles, one per CU), which move half the activation bytes
+// per output element; the backward uses 8-wave 256 x 256 tiles whose two
+// row halves share the decoded weights.  The reduction runs in steps of
 // 64, and inside a step lane-half h of a wave covers the 32 consecutive
 // reduction indices [32h, 32h + 32) -- for the forward exactly one E8M0
 // scale block -- with sub-step kk taking the 8 values 32h + 8kk ..; both
