@@ -102,6 +102,30 @@ def test_random_segments(E, T, N, K, counts):
     check_segments(bf16_values(gx), want_b, offs, what="bwd_x")
 
 
+@pytest.mark.parametrize("E,T,N,K,counts", [
+    # two tiles of 64 reduction steps; 5 uncovered rows
+    (2, 130, 256, 4096, [65, 60]),
+    # 18 tiles x 32 steps, an empty expert
+    (3, 1000, 512, 2048, [300, 0, 650]),
+    # 18 steps (K % 512 != 0), a column tail (264 = 256 + 8)
+    (2, 700, 264, 1152, [350, 300]),
+])
+def test_few_long_tiles(E, T, N, K, counts):
+    """Few output tiles with long reductions (fewer tiles than workgroup
+    slots): oracle parity, zeros past the last expert, and the same bits on a
+    second call."""
+    offs = np.cumsum(counts).astype(np.int32)
+    packed, scales, xb = random_case(E * 7 + K, E, T, N, K, offs)
+    pt, st = gpu_weights(packed, scales)
+    ot = torch.from_numpy(offs).to(dev())
+    xg = to_gpu_bits(xb, "bf16")
+    y = mxq.mxfp4_grouped_mm_fwd(xg, pt, st, ot)
+    want = oracle.grouped_mm_fwd(oracle.from_dtype_bits(xb, "bf16"), packed, scales, offs)
+    check_segments(bf16_values(y), want, offs, what="few long tiles fwd")
+    y2 = mxq.mxfp4_grouped_mm_fwd(xg, pt, st, ot)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
 @pytest.mark.parametrize("raw", [[300, 200, 900], [-5, 150, 40, 10_000]])
 def test_out_of_range_offsets_are_clamped(raw):
     """Offsets that decrease, go negative or pass the row count are clamped
