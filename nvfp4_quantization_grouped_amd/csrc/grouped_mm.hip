@@ -11,10 +11,9 @@
 // Every wave owns a 128-row x 64-column output tile (4 x 2 MFMA tiles, 128
 // fp32 accumulators per lane) and runs two to a SIMD, so one's memory phase
 // overlaps the other's MFMAs.  Forward workgroups of 4 waves (128 x 256
-// tiles, two per CU) serve every shape; large forwards use workgroups of 8
-// waves (128 x 512 tiles, one per CU), which move half the activation bytes
-// per output element; the backward uses 8-wave 256 x 256 tiles whose two
-// row halves share the decoded weights.  The reduction runs in steps of
+// tiles, two per CU) serve every shape; the backward uses 8-wave 256 x 256
+// tiles whose two row halves share the decoded weights.  The reduction runs
+// in steps of
 // 64, and inside a step lane-half h of a wave covers the 32 consecutive
 // reduction indices [32h, 32h + 32) -- for the forward exactly one E8M0
 // scale block -- with sub-step kk taking the 8 values 32h + 8kk ..; both
@@ -25,11 +24,12 @@
 // and which row tile of it its slot is (sum over experts of
 // ceil(rows_e / 128) <= ceil(T / 128) + E slots are launched).  Slots past
 // the last tile zero the rows no expert owns.  No host synchronization.
-// With the default round-robin dispatch of workgroups over the 8 XCDs,
-// column tile x runs on XCD x % 8 for every row slot, so each XCD's L2 keeps
-// the same weight columns hot while the activation blocks it shares with the
-// other XCDs are served from the Infinity Cache (this measured faster than
-// giving each XCD a contiguous range of row slots).
+// With the default round-robin dispatch of workgroups over the 8 XCDs and a
+// multiple of 8 column tiles, column tile x runs on XCD x % 8 for every row
+// slot, so each XCD's L2 keeps the same weight columns hot while the
+// activation blocks it shares with the other XCDs are served from the
+// Infinity Cache (this measured faster than giving each XCD a contiguous
+// range of row slots).
 #include <type_traits>
 
 #include "launch.hpp"
@@ -238,8 +238,9 @@ k_grouped_mm_fwd_general(const uint8_t* __restrict__ a, const uint8_t* __restric
 }
 
 // ------------------------------------------------------ forward, K % 128 == 0
-// Same wave tile and fragment scheme as the general forward, with W = 4 or
-// 8 waves side by side along the columns, and every global transfer of the
+// Same wave tile and fragment scheme as the general forward, with W waves
+// side by side along the columns (W = 4 in use: 128 x 512 tiles of 8 waves,
+// one per CU, measured 2% slower on the routed-expert layer), and every global transfer of the
 // main loop a direct global->LDS DMA (global_load_lds_*), issued two steps
 // ahead into a ring of three LDS stages:
 //  * activations: the 128 x 64 bf16 tile (16 KB) as 16 blocks of 1 KB; a
@@ -766,11 +767,11 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
     const int64_t gy = (tokens + kFwdBM - 1) / kFwdBM + experts;
     if (wk_dim % 128 == 0 && ((uintptr_t)scales & 3) == 0) {
       // scale bytes in 8-step chunks when whole chunks exist (16-byte aligned
-      // rows); 128 x 512 tiles (8 waves) when they still give two per CU
+      // rows); 128 x 256 tiles of 4 waves, two per CU (measured faster on
+      // the routed-expert layer than 128 x 512 tiles of 8 waves, one per CU:
+      // +2% gate/up, +2% down)
       const bool sch8 = wk_dim % 512 == 0 && ((uintptr_t)scales & 15) == 0;
-      const int64_t gx8 = (wn_dim + 511) / 512;
-      const bool wide = gx8 * gy >= 2 * 256;
-      const dim3 g4((unsigned)gx, (unsigned)gy), g8((unsigned)gx8, (unsigned)gy);
+      const dim3 g4((unsigned)gx, (unsigned)gy);
       const bool spread = wk_dim >= 4096;
 #define MXQ_FWD_LAUNCH(W, ST, WG, SCH, SP, G)                                                                \
   hipLaunchKernelGGL((k_grouped_mm_fwd_dma<W, ST, WG, SCH, SP>), G, dim3(W * 64), 0, st, (const uint8_t*)a,  \
@@ -780,9 +781,7 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
     if (spread) MXQ_FWD_LAUNCH(W, ST, WG, SCH, true, G); \
     else MXQ_FWD_LAUNCH(W, ST, WG, SCH, false, G);       \
   } while (0)
-      if (wide && sch8) MXQ_FWD_LAUNCH2(8, 3, 1, 8, g8);
-      else if (wide) MXQ_FWD_LAUNCH2(8, 3, 1, 2, g8);
-      else if (sch8) MXQ_FWD_LAUNCH2(4, 3, 2, 8, g4);
+      if (sch8) MXQ_FWD_LAUNCH2(4, 3, 2, 8, g4);
       else MXQ_FWD_LAUNCH2(4, 3, 2, 2, g4);
 #undef MXQ_FWD_LAUNCH2
 #undef MXQ_FWD_LAUNCH
