@@ -279,7 +279,6 @@ __device__ __forceinline__ void wait_vmcnt_barrier() {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kDmaABytes = kFwdBM * 128;          // 16 KB activation tile per step, unpadded (swizzled)
 
 // LDS of the DMA forward for a workgroup of W waves (W x 64 output columns).
 // A stage holds one step's activation tile and packed weight bytes (32 per
@@ -288,30 +287,32 @@ constexpr int kDmaABytes = kFwdBM * 128;          // 16 KB activation tile per s
 // double buffer of 16 bytes (8 steps) per column, refilled every 8 steps,
 // so the scale transfer touches each column's cache line once per 8 steps
 // instead of once per step.
-template <int W, int SCH>
+template <int BM, int W, int SCH>
 struct DmaStage {                                           // SCH == 8: no scales per stage
-  uint8_t a[kDmaABytes];
+  uint8_t a[BM * 128];                                      // activation tile, unpadded (swizzled)
   uint8_t b[W * 64 * 32];
 };
-template <int W>
-struct DmaStage<W, 2> {
-  uint8_t a[kDmaABytes];
+template <int BM, int W>
+struct DmaStage<BM, W, 2> {
+  uint8_t a[BM * 128];
   uint8_t b[W * 64 * 32];
   uint8_t s[W * 64 * 4];
 };
-template <int W, int STAGES, int SCH>
+template <int BM, int W, int STAGES, int SCH>
 struct DmaSmem {
   static constexpr int kCols = W * 64;
-  static constexpr int kABlocksPerWave = 16 / W;            // 1 KB activation blocks each wave moves
-  using Stage = DmaStage<W, SCH>;
+  static constexpr int kABlocksPerWave = BM / 8 / W;        // 1 KB activation blocks (8 rows) each wave moves
+  static_assert(BM % (8 * W) == 0, "activation blocks per wave");
+  using Stage = DmaStage<BM, W, SCH>;
   Stage st[STAGES];
   uint8_t s8[2][kCols * 16];
 };
-template <int W, int STAGES>
-struct DmaSmem<W, STAGES, 2> {
+template <int BM, int W, int STAGES>
+struct DmaSmem<BM, W, STAGES, 2> {
   static constexpr int kCols = W * 64;
-  static constexpr int kABlocksPerWave = 16 / W;
-  using Stage = DmaStage<W, 2>;
+  static constexpr int kABlocksPerWave = BM / 8 / W;
+  static_assert(BM % (8 * W) == 0, "activation blocks per wave");
+  using Stage = DmaStage<BM, W, 2>;
   Stage st[STAGES];
 };
 
@@ -342,8 +343,8 @@ __device__ __forceinline__ void fwd_dma_issue(StageT& d, const uint8_t* const* a
 }
 
 // The 16-byte scale chunk c (steps 8c .. 8c+7) of this wave's 64 columns.
-template <int W, int STAGES>
-__device__ __forceinline__ void fwd_dma_scales8(DmaSmem<W, STAGES, 8>& sm, const uint8_t* s_src, int wave, int chunk) {
+template <int BM, int W, int STAGES>
+__device__ __forceinline__ void fwd_dma_scales8(DmaSmem<BM, W, STAGES, 8>& sm, const uint8_t* s_src, int wave, int chunk) {
   __builtin_amdgcn_global_load_lds(s_src + 16 * chunk, (lds_void_t*)(sm.s8[chunk & 1] + 1024 * wave), 16, 0, 0);
 }
 
@@ -353,7 +354,7 @@ __device__ __forceinline__ void fwd_dma_scales8(DmaSmem<W, STAGES, 8>& sm, const
 // its own: the compiler keeps LDS writes and reads in order).  Faster for
 // long reductions, slower for short ones (MI355X: +4% at K = 7168 and 4096,
 // -4% at K = 2048).
-template <int W, int STAGES, int MINWG, int SCH, bool SPREAD>
+template <int BM, int W, int STAGES, int MINWG, int SCH, bool SPREAD>
 __global__ void __launch_bounds__(W * 64, MINWG)
 k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
                      const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
@@ -362,8 +363,8 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
   // with SCH == 8 the step-end wait below counts the scale transfer of this
   // step only, which is exact for a ring of three stages
   static_assert(SCH == 2 || STAGES == 3, "scale chunk accounting assumes 3 stages");
-  using Smem = DmaSmem<W, STAGES, SCH>;
-  constexpr int BM = kFwdBM, BN = Smem::kCols, MT = BM / 32, NT = 2, QA = Smem::kABlocksPerWave;
+  using Smem = DmaSmem<BM, W, STAGES, SCH>;
+  constexpr int BN = Smem::kCols, MT = BM / 32, NT = 2, QA = Smem::kABlocksPerWave;
   constexpr int kOps = QA + 2 + (SCH == 2 ? 1 : 0);   // per wave and step (plus 1 every 8 steps when SCH == 8)
   constexpr int kThreads = W * 64;
   const int64_t col0 = (int64_t)blockIdx.x * BN;
@@ -424,7 +425,7 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
   const int nsteps = (int)(kdim / kBK);
   const int last = nsteps - 1;
   const int last_chunk = (nsteps - 1) >> 3;
-  if constexpr (SCH == 8) fwd_dma_scales8<W, STAGES>(sm, s_src, wave, 0);
+  if constexpr (SCH == 8) fwd_dma_scales8<BM, W, STAGES>(sm, s_src, wave, 0);
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t)
     fwd_dma_issue<QA, SCH>(sm.st[t], a_src, b_src, s_src, wave, min(t, last));
@@ -439,7 +440,7 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
     // step's activation and weight transfers (vmcnt counts in issue order)
     const bool chunk_start = SCH == 8 && (s & 7) == 0;
     if constexpr (SCH == 8) {
-      if (chunk_start) fwd_dma_scales8<W, STAGES>(sm, s_src, wave, min((s >> 3) + 1, last_chunk));
+      if (chunk_start) fwd_dma_scales8<BM, W, STAGES>(sm, s_src, wave, min((s >> 3) + 1, last_chunk));
     }
     // refill the stage step s-1 used with step s + STAGES - 1
     typename Smem::Stage& nxt = sm.st[stage == 0 ? STAGES - 1 : stage - 1];
@@ -759,30 +760,49 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
 }
 
 // ------------------------------------------------------------------ launcher
+static int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return n;
+}
+
 hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8_t* packed, const uint8_t* scales,
                              int64_t experts, int64_t wn_dim, int64_t wk_dim, const int32_t* offs, void* out,
                              hipStream_t st) {
   if (!bwd) {
     const int64_t gx = (wn_dim + kFwdBN - 1) / kFwdBN;
-    const int64_t gy = (tokens + kFwdBM - 1) / kFwdBM + experts;
+    const int64_t gy = (tokens + kFwdBM - 1) / kFwdBM + experts;   // 128-row tiles
     if (wk_dim % 128 == 0 && ((uintptr_t)scales & 3) == 0) {
       // scale bytes in 8-step chunks when whole chunks exist (16-byte aligned
       // rows); 128 x 256 tiles of 4 waves, two per CU (measured faster on
       // the routed-expert layer than 128 x 512 tiles of 8 waves, one per CU:
-      // +2% gate/up, +2% down)
+      // +2% gate/up, +2% down).  96-row tiles when they take no more rounds
+      // of two workgroups per CU: the same rounds, each 3/4 as long (a
+      // problem of 288 tiles of 128 rows on 256 CUs leaves 32 CUs running two
+      // while 384 tiles of 96 rows spread evenly)
       const bool sch8 = wk_dim % 512 == 0 && ((uintptr_t)scales & 15) == 0;
-      const dim3 g4((unsigned)gx, (unsigned)gy);
       const bool spread = wk_dim >= 4096;
-#define MXQ_FWD_LAUNCH(W, ST, WG, SCH, SP, G)                                                                \
-  hipLaunchKernelGGL((k_grouped_mm_fwd_dma<W, ST, WG, SCH, SP>), G, dim3(W * 64), 0, st, (const uint8_t*)a,  \
+      const int cus = device_cus();
+      const int64_t slots = 2 * (int64_t)(cus > 0 ? cus : 256);
+      const int64_t gy96 = (tokens + 95) / 96 + experts;
+      const bool bm96 = (gx * gy96 + slots - 1) / slots <= (gx * gy + slots - 1) / slots;
+      const dim3 g128((unsigned)gx, (unsigned)gy), g96((unsigned)gx, (unsigned)gy96);
+#define MXQ_FWD_LAUNCH(BM, SCH, SP, G)                                                                          \
+  hipLaunchKernelGGL((k_grouped_mm_fwd_dma<BM, 4, 3, 2, SCH, SP>), G, dim3(kGemmThreads), 0, st, (const uint8_t*)a, \
                      (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim, (uint8_t*)out)
-#define MXQ_FWD_LAUNCH2(W, ST, WG, SCH, G)        \
-  do {                                            \
-    if (spread) MXQ_FWD_LAUNCH(W, ST, WG, SCH, true, G); \
-    else MXQ_FWD_LAUNCH(W, ST, WG, SCH, false, G);       \
+#define MXQ_FWD_LAUNCH2(BM, SCH, G)                 \
+  do {                                              \
+    if (spread) MXQ_FWD_LAUNCH(BM, SCH, true, G);   \
+    else MXQ_FWD_LAUNCH(BM, SCH, false, G);         \
   } while (0)
-      if (sch8) MXQ_FWD_LAUNCH2(4, 3, 2, 8, g4);
-      else MXQ_FWD_LAUNCH2(4, 3, 2, 2, g4);
+      if (bm96) {
+        if (sch8) MXQ_FWD_LAUNCH2(96, 8, g96);
+        else MXQ_FWD_LAUNCH2(96, 2, g96);
+      } else {
+        if (sch8) MXQ_FWD_LAUNCH2(128, 8, g128);
+        else MXQ_FWD_LAUNCH2(128, 2, g128);
+      }
 #undef MXQ_FWD_LAUNCH2
 #undef MXQ_FWD_LAUNCH
       return hipGetLastError();
