@@ -41,7 +41,7 @@ typedef enum {
   MXQ_ERR_DTYPE = -3,   /* dtype code not supported by this entry point        */
   MXQ_ERR_FORMAT = -4,  /* format code not one of mxq_format                   */
   MXQ_ERR_BLOCK = -5,   /* block_size <= 0                                     */
-  MXQ_ERR_ALIGN = -6,   /* grouped GEMM activation / packed weights not 16-B aligned */
+  MXQ_ERR_ALIGN = -6,   /* grouped GEMM activation / packed weights / output not 16-B aligned */
   MXQ_ERR_ALIAS = -7,   /* output overlaps an input that must stay unmodified  */
   MXQ_ERR_HIP = -8      /* a HIP launch reported an error                      */
 } mxq_status;
@@ -116,7 +116,7 @@ int quantize_cache_bwd(const void* grad_out, void* grad_in, int t, int64_t numel
  * checked on the host (it would need a device sync).  The kernels clamp each
  * offset into [clamped previous offset, tokens], so out-of-range offsets never
  * cause an access past x or y; the result is then that of the clamped offsets.
- * x and packed must be 16-byte aligned; y must not overlap x.
+ * x, packed and y must be 16-byte aligned; y must not overlap x.
  * Errors: MXQ_ERR_NULL, MXQ_ERR_SHAPE (negative sizes, k % 32 != 0 or
  * n % 8 != 0), MXQ_ERR_ALIGN, MXQ_ERR_ALIAS, MXQ_ERR_HIP.
  */

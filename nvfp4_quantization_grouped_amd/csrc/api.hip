@@ -73,7 +73,7 @@ static int grouped_mm_check(const void* a, int64_t tokens, int64_t red, const in
   if (tokens < 0 || red < 0 || other < 0 || experts < 0) return MXQ_ERR_SHAPE;
   if (k % 32 != 0 || n % 8 != 0) return MXQ_ERR_SHAPE;
   if (tokens > 0 && other > 0 && (!a || !out || (experts > 0 && (!packed || !scales || !offs)))) return MXQ_ERR_NULL;
-  if (((uintptr_t)a & 15) || ((uintptr_t)packed & 15)) return MXQ_ERR_ALIGN;
+  if (((uintptr_t)a & 15) || ((uintptr_t)packed & 15) || ((uintptr_t)out & 15)) return MXQ_ERR_ALIGN;
   if (overlap(a, tokens * red * 2, out, tokens * other * 2)) return MXQ_ERR_ALIAS;
   return MXQ_OK;
 }
@@ -112,7 +112,7 @@ const char* mxq_status_string(int s) {
     case MXQ_ERR_DTYPE: return "unsupported dtype";
     case MXQ_ERR_FORMAT: return "unknown format (fp8, mxfp4 or nvfp4)";
     case MXQ_ERR_BLOCK: return "block_size must be positive";
-    case MXQ_ERR_ALIGN: return "misaligned pointer (grouped GEMM operands need 16-byte alignment)";
+    case MXQ_ERR_ALIGN: return "misaligned pointer (grouped GEMM activations, packed weights and output need 16-byte alignment)";
     case MXQ_ERR_ALIAS: return "output overlaps an input";
     case MXQ_ERR_HIP: return "HIP launch error";
     default: return "unknown status";

@@ -76,6 +76,53 @@ __device__ __forceinline__ const uint8_t* packed_e_of(const uint8_t* packed, int
   return packed + (int64_t)e * ndim * (kdim / 2);
 }
 
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+  const f32x2_t v = {x, y};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Output of a wave's MT x 2 tiles of 32 x 32 (a 32*MT x 64 block) through
+// LDS.  The MFMAs compute each tile transposed (weight fragment as the first
+// operand), so lane (r, h) element 4g + e holds row r, column 8g + 4h + e.
+// Per pair of column groups, one v_permlane32_swap per dword trades the
+// halves so lane (r, 0) holds columns 8g..8g+7 and lane (r, 1) columns
+// 8g+8..8g+15 of row r; they go into a row-major LDS block (128 bytes per
+// row, 16-byte chunks XOR-swizzled by (row >> 1) & 7, conflict-free both
+// ways) and come back 16 bytes per lane, 8 lanes per row, so every global
+// store writes 8 whole 128-byte rows (the 2-byte stores of the plain MFMA
+// layout touch each row's cache line in 64-byte halves, 4x as many
+// instructions).  ep: this wave's 32*MT*128 bytes of LDS, free of pending
+// DMA and other waves' reads.  ncols % 8 == 0, ld % 8 == 0, out 16-byte aligned.
+template <int MT>
+__device__ __forceinline__ void store_block_lds(uint8_t* ep, const f32x16_t (&acc)[MT][2], int lane,
+                                                uint8_t* __restrict__ out, int64_t ld, int64_t row0, int64_t row_end,
+                                                int64_t col0, int64_t ncols) {
+  const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g0 = 0; g0 < 4; g0 += 2) {
+        const f32x16_t& c = acc[i][j];
+        const u32x2_t s0 = __builtin_amdgcn_permlane32_swap(pack_bf16x2(c[4 * g0], c[4 * g0 + 1]),
+                                                            pack_bf16x2(c[4 * g0 + 4], c[4 * g0 + 5]), false, false);
+        const u32x2_t s1 = __builtin_amdgcn_permlane32_swap(pack_bf16x2(c[4 * g0 + 2], c[4 * g0 + 3]),
+                                                            pack_bf16x2(c[4 * g0 + 6], c[4 * g0 + 7]), false, false);
+        const int row = 32 * i + r, chunk = 4 * j + g0 + h;
+        *reinterpret_cast<u32x4_t*>(ep + row * 128 + 16 * (chunk ^ ((row >> 1) & 7))) = u32x4_t{s0[0], s1[0], s0[1], s1[1]};
+      }
+#pragma unroll
+  for (int it = 0; it < MT * 4; ++it) {
+    const int row = 8 * it + (lane >> 3), chunk = lane & 7;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ep + row * 128 + 16 * (chunk ^ ((row >> 1) & 7)));
+    const int64_t grow = row0 + row, gcol = col0 + 8 * chunk;
+    if (grow < row_end && gcol < ncols) *reinterpret_cast<u32x4_t*>(out + (grow * ld + gcol) * 2) = v;
+  }
+}
+
 // ---------------------------------------------------------------- A operand
 // A tile: BM rows x 64 bf16 of a row-major [rows, ld] bf16 matrix.
 template <int BM>
@@ -486,7 +533,7 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
       for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j][kk], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j][kk], fa[i], acc[i][j], 0, 0, 0);
     }
     // step s+1 (and its scale chunk) have landed once only the transfers
     // issued after step s+1's may be in flight: steps s+2 .. s+STAGES-1, and
@@ -498,26 +545,12 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
     __builtin_amdgcn_sched_barrier(0);
     stage = stage == STAGES - 1 ? 0 : stage + 1;
   }
-  // drain the clamped tail transfers before this workgroup's LDS is released
+  // drain the clamped tail transfers; once every wave has, the ring is free
   __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
-
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int64_t gc = col0 + wave * 64 + j * 32 + r;
-#pragma unroll
-      for (int q = 0; q < 16; q += 2) {
-        const int64_t gr0 = ti.row0 + i * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
-        f32x2_t v = {acc[i][j][q], acc[i][j][q + 1]};
-        const uint32_t bb = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-        if (wok[j]) {
-          if (gr0 < ti.row_end) *reinterpret_cast<unsigned short*>(out + (gr0 * ndim + gc) * 2) = (unsigned short)(bb & 0xFFFFu);
-          if (gr0 + 1 < ti.row_end) *reinterpret_cast<unsigned short*>(out + ((gr0 + 1) * ndim + gc) * 2) = (unsigned short)(bb >> 16);
-        }
-      }
-    }
-  }
+  __syncthreads();
+  static_assert(sizeof(Smem) >= (size_t)W * BM * 128, "epilogue block fits the ring");
+  store_block_lds<MT>(reinterpret_cast<uint8_t*>(&sm) + wave * BM * 128, acc, lane, out, ndim, ti.row0, ti.row_end,
+                      col0 + wave * 64, ndim);
 }
 
 // ----------------------------------------------------------------- backward
@@ -695,7 +728,7 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
     for (int i = 0; i < MT; ++i)
 #pragma unroll
       for (int j = 0; j < NT; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.fa[i], f.fb[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.fb[j], f.fa[i], acc[i][j], 0, 0, 0);
   };
 
   const int nsteps = (int)((ndim + kBK - 1) / kBK);
@@ -740,23 +773,10 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
     if (s + 1 < nsteps) step(w1, w0, s + 1);
   }
 
-#pragma unroll
-  for (int i = 0; i < MT; ++i) {
-#pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int64_t gc = col0 + wn * 64 + j * 32 + r;
-#pragma unroll
-      for (int q = 0; q < 16; q += 2) {
-        const int64_t gr0 = ti.row0 + 128 * wm + i * 32 + 8 * (q >> 2) + 4 * h + (q & 3);
-        f32x2_t v = {acc[i][j][q], acc[i][j][q + 1]};
-        const uint32_t bb = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-        if (gc < kdim) {
-          if (gr0 < ti.row_end) *reinterpret_cast<unsigned short*>(out + (gr0 * kdim + gc) * 2) = (unsigned short)(bb & 0xFFFFu);
-          if (gr0 + 1 < ti.row_end) *reinterpret_cast<unsigned short*>(out + ((gr0 + 1) * kdim + gc) * 2) = (unsigned short)(bb >> 16);
-        }
-      }
-    }
-  }
+  // the last step's barrier has retired every read of the tiles
+  static_assert(sizeof(BwdSmem) >= (size_t)8 * 128 * 128, "epilogue block fits");
+  store_block_lds<MT>(reinterpret_cast<uint8_t*>(&sm) + wave * 128 * 128, acc, lane, out, kdim, ti.row0 + 128 * wm,
+                      ti.row_end, col0 + wn * 64, kdim);
 }
 
 // ------------------------------------------------------------------ launcher

@@ -88,6 +88,7 @@ def test_grouped_mm_validation(L):
     assert f(FAKE, 16, 64, FAKE * 2, FAKE * 3, 2, 60, FAKE * 4, FAKE * 5, None) == -2    # n % 8
     assert f(FAKE, 16, 64, None, FAKE * 3, 2, 64, FAKE * 4, FAKE * 5, None) == -1
     assert f(FAKE + 2, 16, 64, FAKE * 2, FAKE * 3, 2, 64, FAKE * 4, FAKE * 5, None) == -6  # alignment
+    assert f(FAKE, 16, 64, FAKE * 2, FAKE * 3, 2, 64, FAKE * 4, FAKE * 5 + 8, None) == -6  # output alignment
     assert f(FAKE, 16, 64, FAKE * 2, FAKE * 3, 2, 64, FAKE * 4, FAKE + 64, None) == -7   # y overlaps x
     assert f(FAKE, 0, 64, FAKE * 2, FAKE * 3, 2, 64, FAKE * 4, FAKE * 5, None) == 0      # no tokens
     b = L.mxfp4_grouped_mm_bwd_x
