@@ -363,36 +363,53 @@ struct DmaSmem<BM, W, STAGES, 2> {
   Stage st[STAGES];
 };
 
+// Global sides of one wave's transfers, as raw buffers: the descriptors
+// (scalar registers) hold the tile's, or the wave's, first row and the
+// valid range, each lane a fixed 32-bit offset, and a step only moves the
+// scalar offset, so no vector address arithmetic runs per transfer; reads
+// past the range (rows past the expert's end, weight rows past n) return
+// zeros.
+template <int QA>
+struct DmaSrc {
+  __amdgpu_buffer_rsrc_t a, b, s;   // activations, packed weights, scales
+  uint32_t a_off[QA];
+  uint32_t b_off[2];
+  uint32_t s_off;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(bytes > 0 ? bytes : 0), 0x00020000);
+}
+
 // Op q of one step's transfers of one wave, straight into LDS (q < QA:
 // activation block q; then the 2 weight blocks; then, with SCH == 2, the
 // scale dword).
 template <int QA, int SCH, class StageT>
-__device__ __forceinline__ void fwd_dma_op(StageT& d, const uint8_t* const* a_src, const uint8_t* const* b_src,
-                                           const uint8_t* s_src, int wave, int step, int q) {
+__device__ __forceinline__ void fwd_dma_op(StageT& d, const DmaSrc<QA>& src, int wave, int step, int q) {
   if (q < QA) {
-    __builtin_amdgcn_global_load_lds(a_src[q] + (int64_t)step * kBK * 2, (lds_void_t*)(d.a + 1024 * (QA * wave + q)),
-                                     16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.a, (lds_void_t*)(d.a + 1024 * (QA * wave + q)), 16, src.a_off[q],
+                                             step * kBK * 2, 0, 0);
   } else if (q < QA + 2) {
     const int j = q - QA;
-    __builtin_amdgcn_global_load_lds(b_src[j] + (int64_t)step * 32, (lds_void_t*)(d.b + 2048 * wave + 1024 * j), 16,
-                                     0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.b, (lds_void_t*)(d.b + 2048 * wave + 1024 * j), 16, src.b_off[j],
+                                             step * 32, 0, 0);
   } else if constexpr (SCH == 2) {
-    __builtin_amdgcn_global_load_lds(s_src + 4 * (step >> 1), (lds_void_t*)(d.s + 256 * wave), 4, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.s, (lds_void_t*)(d.s + 256 * wave), 4, src.s_off, 4 * (step >> 1), 0,
+                                             0);
   }
 }
 
 // All of one step's transfers of one wave.
 template <int QA, int SCH, class StageT>
-__device__ __forceinline__ void fwd_dma_issue(StageT& d, const uint8_t* const* a_src, const uint8_t* const* b_src,
-                                              const uint8_t* s_src, int wave, int step) {
+__device__ __forceinline__ void fwd_dma_issue(StageT& d, const DmaSrc<QA>& src, int wave, int step) {
 #pragma unroll
-  for (int q = 0; q < QA + 2 + (SCH == 2 ? 1 : 0); ++q) fwd_dma_op<QA, SCH>(d, a_src, b_src, s_src, wave, step, q);
+  for (int q = 0; q < QA + 2 + (SCH == 2 ? 1 : 0); ++q) fwd_dma_op<QA, SCH>(d, src, wave, step, q);
 }
 
-// The 16-byte scale chunk c (steps 8c .. 8c+7) of this wave's 64 columns.
-template <int BM, int W, int STAGES>
-__device__ __forceinline__ void fwd_dma_scales8(DmaSmem<BM, W, STAGES, 8>& sm, const uint8_t* s_src, int wave, int chunk) {
-  __builtin_amdgcn_global_load_lds(s_src + 16 * chunk, (lds_void_t*)(sm.s8[chunk & 1] + 1024 * wave), 16, 0, 0);
+// The 16-byte scale chunk c (steps 8c .. 8c+7) of this wave's 64 columns,
+// into dst (this wave's 1 KB of the chunk's buffer).
+__device__ __forceinline__ void fwd_dma_scales8(lds_void_t* dst, __amdgpu_buffer_rsrc_t s, uint32_t s_off, int chunk) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(s, dst, 16, s_off, 16 * chunk, 0, 0);
 }
 
 // SPREAD: issue a step's transfers one or two at a time behind each
@@ -417,7 +434,8 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
   const int64_t col0 = (int64_t)blockIdx.x * BN;
   const TileInfo ti = find_tile<BM>(offs, experts, tokens, blockIdx.y);
   if (ti.expert == -2) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave index in a scalar register: the LDS destinations of the DMA are scalar
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, r = lane & 31;
 
   if (ti.expert == -1) {
@@ -436,32 +454,25 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
 
   // activation DMA: this wave fills A blocks QA*wave .. QA*wave+QA-1; block b
   // holds rows 8b .. 8b+7: lane l -> row 8b + l/8, LDS chunk l%8 <- global
-  // chunk (l%8) ^ ((row >> 1) & 7)
-  const uint8_t* a_src[QA];
+  // chunk (l%8) ^ ((row >> 1) & 7).  Ranges and offsets fit 31 bits (the
+  // launcher checks BM * K * 2 and one expert's packed weights).
+  DmaSrc<QA> src;
+  src.a = dma_rsrc(a + ti.row0 * kdim * 2, (ti.row_end - ti.row0) * kdim * 2);
 #pragma unroll
   for (int q = 0; q < QA; ++q) {
     const int row = 8 * (QA * wave + q) + (lane >> 3);
-    int64_t grow = ti.row0 + row;
-    if (grow >= ti.row_end) grow = ti.row_end - 1;
-    a_src[q] = a + (grow * kdim + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2;
+    src.a_off[q] = (uint32_t)(((int64_t)row * kdim + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2);
   }
   // weight DMA: this wave's rows n = col0 + 64*wave + 32*j + r (j = 0, 1);
   // block j holds [half h][row r] x 16 bytes.  Scales: lane l covers column
   // 64*wave + l (a dword per step pair, or 16 bytes per 8 steps).
-  const uint8_t* packed_e = packed_e_of(packed, ti.expert, ndim, kdim);
-  const uint8_t* b_src[NT];
-  bool wok[NT];
+  const int64_t n0 = col0 + wave * 64;
+  src.b = dma_rsrc(packed_e_of(packed, ti.expert, ndim, kdim) + n0 * (kdim / 2), (ndim - n0) * (kdim / 2));
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
-    int64_t n = col0 + wave * 64 + j * 32 + r;
-    wok[j] = n < ndim;
-    if (!wok[j]) n = ndim - 1;
-    b_src[j] = packed_e + n * (kdim / 2) + 16 * h;
-  }
-  int64_t n_s = col0 + wave * 64 + lane;
-  if (n_s >= ndim) n_s = ndim - 1;
+  for (int j = 0; j < NT; ++j) src.b_off[j] = (uint32_t)((j * 32 + r) * (kdim / 2) + 16 * h);
   // 4-byte aligned rows for SCH == 2 (K % 128 == 0), 16-byte for SCH == 8 (K % 512 == 0)
-  const uint8_t* s_src = scales + ((int64_t)ti.expert * ndim + n_s) * (kdim / 32);
+  src.s = dma_rsrc(scales + ((int64_t)ti.expert * ndim + n0) * (kdim / 32), (ndim - n0) * (kdim / 32));
+  src.s_off = (uint32_t)(lane * (kdim / 32));
 
   f32x16_t acc[MT][NT];
 #pragma unroll
@@ -472,10 +483,10 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
   const int nsteps = (int)(kdim / kBK);
   const int last = nsteps - 1;
   const int last_chunk = (nsteps - 1) >> 3;
-  if constexpr (SCH == 8) fwd_dma_scales8<BM, W, STAGES>(sm, s_src, wave, 0);
+  if constexpr (SCH == 8) fwd_dma_scales8((lds_void_t*)(sm.s8[0] + 1024 * wave), src.s, src.s_off, 0);
 #pragma unroll
   for (int t = 0; t < STAGES - 1; ++t)
-    fwd_dma_issue<QA, SCH>(sm.st[t], a_src, b_src, s_src, wave, min(t, last));
+    fwd_dma_issue<QA, SCH>(sm.st[t], src, wave, min(t, last));
   // step 0 (and scale chunk 0) have landed once only steps 1 .. STAGES-2 may be in flight
   wait_vmcnt_barrier<kOps * (STAGES - 2)>();
 
@@ -487,12 +498,15 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
     // step's activation and weight transfers (vmcnt counts in issue order)
     const bool chunk_start = SCH == 8 && (s & 7) == 0;
     if constexpr (SCH == 8) {
-      if (chunk_start) fwd_dma_scales8<BM, W, STAGES>(sm, s_src, wave, min((s >> 3) + 1, last_chunk));
+      if (chunk_start) {
+        const int c = min((s >> 3) + 1, last_chunk);
+        fwd_dma_scales8((lds_void_t*)(sm.s8[c & 1] + 1024 * wave), src.s, src.s_off, c);
+      }
     }
     // refill the stage step s-1 used with step s + STAGES - 1
     typename Smem::Stage& nxt = sm.st[stage == 0 ? STAGES - 1 : stage - 1];
     const int nstep = min(s + STAGES - 1, last);
-    if constexpr (!SPREAD) fwd_dma_issue<QA, SCH>(nxt, a_src, b_src, s_src, wave, nstep);
+    if constexpr (!SPREAD) fwd_dma_issue<QA, SCH>(nxt, src, wave, nstep);
     const typename Smem::Stage& c = sm.st[stage];
     // decode this wave's weights for the step into B fragments
     bf16x8_t fb[NT][4];
@@ -527,7 +541,7 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
         constexpr int kOpsAll = QA + 2 + (SCH == 2 ? 1 : 0);
 #pragma unroll
         for (int q = kk * kOpsAll / 4; q < (kk + 1) * kOpsAll / 4; ++q)
-          fwd_dma_op<QA, SCH>(nxt, a_src, b_src, s_src, wave, nstep, q);
+          fwd_dma_op<QA, SCH>(nxt, src, wave, nstep, q);
       }
 #pragma unroll
       for (int i = 0; i < MT; ++i)
@@ -793,7 +807,8 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
   if (!bwd) {
     const int64_t gx = (wn_dim + kFwdBN - 1) / kFwdBN;
     const int64_t gy = (tokens + kFwdBM - 1) / kFwdBM + experts;   // 128-row tiles
-    if (wk_dim % 128 == 0 && ((uintptr_t)scales & 3) == 0) {
+    if (wk_dim % 128 == 0 && wk_dim < (int64_t(1) << 22) && wn_dim * (wk_dim / 2) < (int64_t(1) << 31) &&
+        ((uintptr_t)scales & 3) == 0) {
       // scale bytes in 8-step chunks when whole chunks exist (16-byte aligned
       // rows); 128 x 256 tiles of 4 waves, two per CU (measured faster on
       // the routed-expert layer than 128 x 512 tiles of 8 waves, one per CU:
