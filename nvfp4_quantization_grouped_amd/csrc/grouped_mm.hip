@@ -658,14 +658,18 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
   const uint32_t g_off0 = (uint32_t)((threadIdx.x >> 3) * ndim + g_col) * 2;
   const uint32_t g_row_step = (uint32_t)(64 * ndim * 2);
   u32x4_t gr_regs[GC];
+  // the step moves the scalar offset only; lane offsets are fixed
+  uint32_t g_voff[GC];
+#pragma unroll
+  for (int i = 0; i < GC; ++i) g_voff[i] = g_off0 + i * g_row_step;
   auto load_g = [&](int64_t n0) {
     // N % 8 == 0: a chunk is wholly in or out of range
     const bool ok = n0 + g_col < ndim;
-    const uint32_t base = g_off0 + (uint32_t)(n0 * 2);
+    const uint32_t soff = (uint32_t)(min(n0, ndim) * 2);
 #pragma unroll
     for (int i = 0; i < GC; ++i)
-      gr_regs[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   rs_g, ok ? base + i * g_row_step : kBufOob, 0, 0));
+      gr_regs[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_g, ok ? g_voff[i] : kBufOob,
+                                                                                     soff, 0));
   };
   // (row >> 1) & 7 of the rows t / 8 + 64 i does not depend on i
   const int g_st = (threadIdx.x >> 3) * 128 + 16 * ((threadIdx.x & 7) ^ ((threadIdx.x >> 4) & 7));
@@ -682,12 +686,13 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
   const __amdgpu_buffer_rsrc_t rs_w = buf_rsrc(packed_e_of(packed, ti.expert, ndim, kdim), ndim * prow);
   const __amdgpu_buffer_rsrc_t rs_s = buf_rsrc(scales + (int64_t)ti.expert * ndim * srow, ndim * srow);
   const uint32_t wcol = (uint32_t)(kc / 2 + 16 * whalf), scol = (uint32_t)(kc / 32 + whalf);
+  const uint32_t w_voff = (uint32_t)(wrow * prow) + wcol, s_voff = (uint32_t)(wrow * srow) + scol;
   auto load_w = [&](WRaw& w, int64_t n0) {
-    const int64_t n = n0 + wrow;
-    const bool ok = wvalid && n < ndim;
-    w.pk = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rs_w, ok ? (uint32_t)(n * prow) + wcol : kBufOob, 0, 0));
-    w.sb = __builtin_amdgcn_raw_buffer_load_b8(rs_s, ok ? (uint32_t)(n * srow) + scol : kBufOob, 0, 0);
+    const bool ok = wvalid && n0 + wrow < ndim;
+    const int64_t nc = min(n0, ndim);   // scalar offsets stay below the range (no 32-bit wrap)
+    w.pk = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs_w, ok ? w_voff : kBufOob,
+                                                                             (uint32_t)(nc * prow), 0));
+    w.sb = __builtin_amdgcn_raw_buffer_load_b8(rs_s, ok ? s_voff : kBufOob, (uint32_t)(nc * srow), 0);
   };
   const int wd_st = wrow * 128, wd_swz_row = wd_swz(wrow);
   // decode a piece (32 values) and write it into Wd, 16 bytes at a time
