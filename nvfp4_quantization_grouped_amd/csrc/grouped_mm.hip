@@ -29,7 +29,9 @@
 // slot, so each XCD's L2 keeps the same weight columns hot while the
 // activation blocks it shares with the other XCDs are served from the
 // Infinity Cache (this measured faster than giving each XCD a contiguous
-// range of row slots).
+// range of row slots).  The backward remaps its workgroups the other way
+// (an XCD takes whole row slots with all their column tiles): its grad_out
+// tiles are the larger operand to re-fetch, and this measured 2-4% faster.
 #include <type_traits>
 
 #include "launch.hpp"
@@ -631,8 +633,13 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
                  int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out) {
   constexpr int BM = kBwdBM, BN = kBwdBN, MT = 4, NT = 2, kThreads = kBwdThreads;
   constexpr int GC = BM * 8 / kThreads;                // 16-byte grad_out chunks per thread and step
-  const int64_t col0 = (int64_t)blockIdx.x * BN;
-  const TileInfo ti = find_tile<BM>(offs, experts, tokens, blockIdx.y);
+  // XCD-major remap: the workgroups the round-robin dispatch puts on XCD x
+  // (linear id % 8 == x) take row slots x, x + 8, ..., each with all its
+  // column tiles, so a row tile's grad_out is fetched into one L2 only
+  const int64_t lin = (int64_t)blockIdx.y * gridDim.x + blockIdx.x, kx = lin >> 3;
+  const int slot_y = (int)((kx / gridDim.x) * 8 + (lin & 7));
+  const int64_t col0 = (int64_t)(kx % gridDim.x) * BN;
+  const TileInfo ti = find_tile<BM>(offs, experts, tokens, slot_y);
   if (ti.expert == -2) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 2, wn = wave & 3;
@@ -854,7 +861,7 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
   }
   {
     const int64_t gx = (wk_dim + kBwdBN - 1) / kBwdBN;
-    const int64_t gy = (tokens + kBwdBM - 1) / kBwdBM + experts;
+    const int64_t gy = ((tokens + kBwdBM - 1) / kBwdBM + experts + 7) / 8 * 8;
     hipLaunchKernelGGL(k_grouped_mm_bwd, dim3((unsigned)gx, (unsigned)gy), dim3(kBwdThreads), 0, st,
                        (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim,
                        (uint8_t*)out);
