@@ -417,9 +417,10 @@ __device__ __forceinline__ void fwd_dma_scales8(lds_void_t* dst, __amdgpu_buffer
 // SPREAD: issue a step's transfers one or two at a time behind each
 // sub-step's fragment reads, so they go out between MFMAs instead of as one
 // burst ahead of them (a transfer cannot move past LDS reads of the ring on
-// its own: the compiler keeps LDS writes and reads in order).  Faster for
-// long reductions, slower for short ones (MI355X: +4% at K = 7168 and 4096,
-// -4% at K = 2048).
+// its own: the compiler keeps LDS writes and reads in order).  With buffer
+// transfers it is as fast or faster at every K measured (MI355X: +3% at
+// K = 7168, +2% at K = 2048); the burst form (SPREAD = false) is kept as
+// the reference schedule.
 template <int BM, int W, int STAGES, int MINWG, int SCH, bool SPREAD>
 __global__ void __launch_bounds__(W * 64, MINWG)
 k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
@@ -829,28 +830,21 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
       // problem of 288 tiles of 128 rows on 256 CUs leaves 32 CUs running two
       // while 384 tiles of 96 rows spread evenly)
       const bool sch8 = wk_dim % 512 == 0 && ((uintptr_t)scales & 15) == 0;
-      const bool spread = wk_dim >= 4096;
       const int cus = device_cus();
       const int64_t slots = 2 * (int64_t)(cus > 0 ? cus : 256);
       const int64_t gy96 = (tokens + 95) / 96 + experts;
       const bool bm96 = (gx * gy96 + slots - 1) / slots <= (gx * gy + slots - 1) / slots;
       const dim3 g128((unsigned)gx, (unsigned)gy), g96((unsigned)gx, (unsigned)gy96);
-#define MXQ_FWD_LAUNCH(BM, SCH, SP, G)                                                                          \
-  hipLaunchKernelGGL((k_grouped_mm_fwd_dma<BM, 4, 3, 2, SCH, SP>), G, dim3(kGemmThreads), 0, st, (const uint8_t*)a, \
+#define MXQ_FWD_LAUNCH(BM, SCH, G)                                                                                \
+  hipLaunchKernelGGL((k_grouped_mm_fwd_dma<BM, 4, 3, 2, SCH, true>), G, dim3(kGemmThreads), 0, st, (const uint8_t*)a, \
                      (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim, (uint8_t*)out)
-#define MXQ_FWD_LAUNCH2(BM, SCH, G)                 \
-  do {                                              \
-    if (spread) MXQ_FWD_LAUNCH(BM, SCH, true, G);   \
-    else MXQ_FWD_LAUNCH(BM, SCH, false, G);         \
-  } while (0)
       if (bm96) {
-        if (sch8) MXQ_FWD_LAUNCH2(96, 8, g96);
-        else MXQ_FWD_LAUNCH2(96, 2, g96);
+        if (sch8) MXQ_FWD_LAUNCH(96, 8, g96);
+        else MXQ_FWD_LAUNCH(96, 2, g96);
       } else {
-        if (sch8) MXQ_FWD_LAUNCH2(128, 8, g128);
-        else MXQ_FWD_LAUNCH2(128, 2, g128);
+        if (sch8) MXQ_FWD_LAUNCH(128, 8, g128);
+        else MXQ_FWD_LAUNCH(128, 2, g128);
       }
-#undef MXQ_FWD_LAUNCH2
 #undef MXQ_FWD_LAUNCH
       return hipGetLastError();
     }
