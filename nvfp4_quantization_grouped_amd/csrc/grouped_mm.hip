@@ -587,10 +587,9 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
 //    32) of the step's 64 in its 64 columns -- one piece of 16 packed bytes
 //    (32 values of one row) and its scale byte per lane -- decodes it along
 //    k (the direction the scaled fp4 conversion and the E8M0 block both run)
-//    once the previous step's MFMAs are issued, so the conversions overlap
-//    their execution, and writes it in 16-byte chunks into the column
-//    block's tile Wd[n][k] of the next step (double-buffered, so the barrier
-//    that ends the step publishes it);
+//    a step later, between that step's MFMAs, and writes it in 16-byte
+//    chunks into the column block's tile Wd[n][k] of the step after
+//    (double-buffered, so the barrier that ends the step publishes it);
 //  * the B fragments, which need 8 consecutive n of one column per lane,
 //    come out of Wd with gfx950's transposing LDS read ds_read_b64_tr_b16:
 //    within each group of 16 lanes, output lane i, element e is element
@@ -770,10 +769,12 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
   // sub-step's fragments read one sub-step ahead.  All waves reach the LDS
   // at once after the barrier, so the first fragment reads go out before
   // the next step's global loads: grad_out of step s + 1 (through registers
-  // into the other tile at the end of the step) and the raw weights of step
-  // s + 2 (into `nxt`).  `cur` holds the raw weights of step s + 1, fetched
-  // a step earlier and decoded into the other Wd buffer behind the MFMAs.
-  // Loads past the last step read zeros.
+  // into the other tile, stored behind sub-step 2) and the raw weights of
+  // step s + 2 (into `nxt`).  `cur` holds the raw weights of step s + 1,
+  // fetched a step earlier and decoded into the other Wd buffer behind
+  // sub-step 1.  Both buffers of step s + 1 were last read in step s - 1,
+  // so the barrier that ends step s is the only one.  Loads past the last
+  // step read zeros.
   auto step = [&](WRaw& cur, WRaw& nxt, int s) {
     const uint8_t* la = sm.g[s & 1] + (128 * wm + r) * 128;
     const uint8_t* wd = sm.w[s & 1][wn];
@@ -789,10 +790,14 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
         load_w(nxt, (int64_t)(s + 2) * kBK);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (kk == 1) put_piece(cur, sm.w[(s & 1) ^ 1][wn]);
+      if (kk == 2) {
+        // the grad_out loads issued after sub-step 0 have had two sub-steps
+        __builtin_amdgcn_sched_barrier(0);
+        store_g(sm.g[(s & 1) ^ 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    put_piece(cur, sm.w[(s & 1) ^ 1][wn]);
-    __builtin_amdgcn_sched_barrier(0);
-    store_g(sm.g[(s & 1) ^ 1]);
     __syncthreads();
   };
   for (int s = 0; s < nsteps; s += 2) {
