@@ -289,10 +289,12 @@ k_grouped_mm_fwd_general(const uint8_t* __restrict__ a, const uint8_t* __restric
 // ------------------------------------------------------ forward, K % 128 == 0
 // Same wave tile and fragment scheme as the general forward, with W waves
 // side by side along the columns (W = 4 in use: 128 x 512 tiles of 8 waves,
-// one per CU, measured 2% slower on the routed-expert layer), and every global transfer of the
-// main loop a direct global->LDS DMA (global_load_lds_*), issued two steps
-// ahead into a ring of three LDS stages:
-//  * activations: the 128 x 64 bf16 tile (16 KB) as 16 blocks of 1 KB; a
+// one per CU, measured 2% slower on the routed-expert layer) and BM = 128 or
+// 96 rows, and every global transfer of the main loop a direct global->LDS
+// DMA (buffer_load ... lds: the buffer descriptor carries the row base and
+// the valid range, the scalar offset the step), issued two steps ahead into
+// a ring of three LDS stages:
+//  * activations: the BM x 64 bf16 tile as BM / 8 blocks of 1 KB; a
 //    block holds 8 rows, and within a row the eight 16-byte chunks are
 //    XOR-swizzled by ((row >> 1) & 7): LDS serves 16 lanes x 16 bytes (256
 //    bytes, two 128-byte rows) per cycle, and with this swizzle any 16
@@ -313,8 +315,8 @@ k_grouped_mm_fwd_general(const uint8_t* __restrict__ a, const uint8_t* __restric
 // The step index of the prefetch is clamped at the end, so every iteration
 // issues the same operations (keeping N constant); the surplus transfers are
 // in-bounds and land in a stage nobody reads.  Rows past the expert's segment
-// load a clamped valid row and are never stored; weight rows past N
-// likewise.  Needs K % 128 == 0 (4-byte aligned scale rows).
+// and weight rows past N lie past their buffer's range and read zeros; they
+// are never stored.  Needs K % 128 == 0 (4-byte aligned scale rows).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
