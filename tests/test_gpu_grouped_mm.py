@@ -145,6 +145,24 @@ def test_out_of_range_offsets_are_clamped(raw):
     check_segments(bf16_values(gx), want_b, clamped, what="bwd_x clamped offs")
 
 
+def test_very_long_reduction():
+    """K = 2^22: past the 32-bit buffer ranges of the DMA forward, so the
+    forward takes the general kernel; grad_x (reduction over n = 16) covers
+    16384 column tiles.  Parity with the oracle both ways."""
+    E, T, N, K = 1, 3, 16, 1 << 22
+    offs = np.array([T], np.int32)
+    packed, scales, xb = random_case(99, E, T, N, K, offs)
+    pt, st = gpu_weights(packed, scales)
+    ot = torch.from_numpy(offs).to(dev())
+    y = mxq.mxfp4_grouped_mm_fwd(to_gpu_bits(xb, "bf16"), pt, st, ot)
+    want = oracle.grouped_mm_fwd(oracle.from_dtype_bits(xb, "bf16"), packed, scales, offs)
+    check_segments(bf16_values(y), want, offs, what="K = 2^22 fwd")
+    gb = synth.normal_bf16(np.random.default_rng(3), (T, N), 0.1)
+    gx = mxq.mxfp4_grouped_mm_bwd_x(to_gpu_bits(gb, "bf16"), pt, st, ot)
+    want_b = oracle.grouped_mm_bwd_x(oracle.from_dtype_bits(gb, "bf16"), packed, scales, offs)
+    check_segments(bf16_values(gx), want_b, offs, what="K = 2^22 bwd_x")
+
+
 def test_autograd_function():
     E, T, N, K = 4, 400, 256, 512
     offs = np.array([100, 200, 300, 400], np.int32)
