@@ -312,11 +312,11 @@ k_grouped_mm_fwd_general(const uint8_t* __restrict__ a, const uint8_t* __restric
 //  * each step waits for exactly the DMA of the step it is about to use
 //    (s_waitcnt vmcnt(N), N = operations issued after it), then barriers.
 // With no register-destined loads in the loop, no other waits are needed.
-// The step index of the prefetch is clamped at the end, so every iteration
-// issues the same operations (keeping N constant); the surplus transfers are
-// in-bounds and land in a stage nobody reads.  Rows past the expert's segment
-// and weight rows past N lie past their buffer's range and read zeros; they
-// are never stored.  Needs K % 128 == 0 (4-byte aligned scale rows).
+// Every step but the last STAGES - 1 issues the same operations (keeping N
+// constant); those last steps issue none and wait for everything pending.
+// Rows past the expert's segment and weight rows past N lie past their
+// buffer's range and read zeros; they are never stored.  Needs K % 128 == 0
+// (4-byte aligned scale rows).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -508,10 +508,14 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
         fwd_dma_scales8((lds_void_t*)(sm.s8[c & 1] + 1024 * wave), src.s, src.s_off, c);
       }
     }
-    // refill the stage step s-1 used with step s + STAGES - 1
+    // refill the stage step s-1 used with step s + STAGES - 1 (none in the
+    // last STAGES - 1 steps: nothing is left to fetch)
     typename Smem::Stage& nxt = sm.st[stage == 0 ? STAGES - 1 : stage - 1];
-    const int nstep = min(s + STAGES - 1, last);
-    if constexpr (!SPREAD) fwd_dma_issue<QA, SCH>(nxt, src, wave, nstep);
+    const int nstep = s + STAGES - 1;
+    const bool refill = nstep <= last;
+    if constexpr (!SPREAD) {
+      if (refill) fwd_dma_issue<QA, SCH>(nxt, src, wave, nstep);
+    }
     const typename Smem::Stage& c = sm.st[stage];
     // decode this wave's weights for the step into B fragments
     bf16x8_t fb[NT][4];
@@ -544,9 +548,11 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
         // this sub-step's share of the next stage's transfers (same ops, same
         // order, so the step-end vmcnt count is unchanged)
         constexpr int kOpsAll = QA + 2 + (SCH == 2 ? 1 : 0);
+        if (refill) {
 #pragma unroll
-        for (int q = kk * kOpsAll / 4; q < (kk + 1) * kOpsAll / 4; ++q)
-          fwd_dma_op<QA, SCH>(nxt, src, wave, nstep, q);
+          for (int q = kk * kOpsAll / 4; q < (kk + 1) * kOpsAll / 4; ++q)
+            fwd_dma_op<QA, SCH>(nxt, src, wave, nstep, q);
+        }
       }
 #pragma unroll
       for (int i = 0; i < MT; ++i)
@@ -557,7 +563,9 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
     // step s+1 (and its scale chunk) have landed once only the transfers
     // issued after step s+1's may be in flight: steps s+2 .. s+STAGES-1, and
     // this step's scale chunk
-    if (chunk_start)
+    if (!refill)
+      wait_vmcnt_barrier<0>();   // nothing issued this step: all that is pending is needed
+    else if (chunk_start)
       wait_vmcnt_barrier<kOps * (STAGES - 2) + 1>();
     else
       wait_vmcnt_barrier<kOps * (STAGES - 2)>();
