@@ -118,7 +118,9 @@ int quantize_cache_bwd(const void* grad_out, void* grad_in, int t, int64_t numel
  * cause an access past x or y; the result is then that of the clamped offsets.
  * x, packed and y must be 16-byte aligned; y must not overlap x.
  * Errors: MXQ_ERR_NULL, MXQ_ERR_SHAPE (negative sizes, k % 32 != 0 or
- * n % 8 != 0), MXQ_ERR_ALIGN, MXQ_ERR_ALIAS, MXQ_ERR_HIP.
+ * n % 8 != 0), MXQ_ERR_ALIGN, MXQ_ERR_ALIAS, MXQ_ERR_HIP (also when the
+ * launch would pass 2^24 output tiles of 128 x 256, a hardware grid limit:
+ * about tokens * n > 5.5e11).
  */
 int mxfp4_grouped_mm_fwd(const void* x, int64_t tokens, int64_t k,
                          const int8_t* packed, const uint8_t* scales, int64_t experts, int64_t n,
@@ -131,7 +133,8 @@ int mxfp4_grouped_mm_fwd(const void* x, int64_t tokens, int64_t k,
  * a fresh on-the-fly dequantization; no weight gradient (frozen base).
  * Rows past offs[experts-1] are written as zeros.  Same preconditions and
  * errors as the forward; also MXQ_ERR_SHAPE when n > 2^22 or one expert's
- * packed weights reach 2 GiB (n * k / 2 >= 2^31).
+ * packed weights reach 2 GiB (n * k / 2 >= 2^31), and MXQ_ERR_HIP past 2^23
+ * output tiles of 256 x 256 (about tokens * k > 5.5e11).
  */
 int mxfp4_grouped_mm_bwd_x(const void* grad_out, int64_t tokens, int64_t n,
                            const int8_t* packed, const uint8_t* scales, int64_t experts, int64_t k,

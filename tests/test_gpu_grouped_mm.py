@@ -163,6 +163,49 @@ def test_very_long_reduction():
     check_segments(bf16_values(gx), want_b, offs, what="K = 2^22 bwd_x")
 
 
+def test_expert_segment_past_4gib():
+    """One expert owning 2^24 + 16 rows: its activation segment (K = 128) and
+    grad_out segment (N = 128) span 2^32 + 4096 bytes, past any 32-bit
+    buffer range, and each row tile must still read its own 128 or 256 rows
+    (a range taken over the whole segment would wrap to 4 KB and read zeros
+    from row 16 on).  The rows repeat a seeded 4096-row block, so the oracle
+    takes the sampled rows from the block: the first tiles, the middle and
+    the last rows, both ways."""
+    T = (1 << 24) + 16
+    rows = np.concatenate([np.arange(0, 512), (1 << 23) + np.arange(0, 256), np.arange(T - 300, T)])
+    offs = np.array([T], np.int32)
+    ot = torch.from_numpy(offs).to(dev())
+    d = synth.streams(41, 6)
+
+    def tiled(block):
+        t = to_gpu_bits(block, "bf16")
+        return t.repeat(T // block.shape[0] + 1, 1)[:T].contiguous()
+
+    # forward: x [T, 128] -> y [T, 8]
+    K, N = 128, 8
+    packed, scales = synth.packed_weights(d[0], d[1], 1, N, K)
+    xb = synth.normal_bf16(d[2], (4096, K))
+    pt, st = gpu_weights(packed, scales)
+    x = tiled(xb)
+    y = from_gpu_bits(mxq.mxfp4_grouped_mm_fwd(x, pt, st, ot)[torch.from_numpy(rows).to(dev())])
+    del x
+    want = oracle.grouped_mm_fwd(oracle.from_dtype_bits(xb[rows % 4096], "bf16"), packed, scales,
+                                 np.array([len(rows)], np.int32))
+    check_segments(oracle.from_dtype_bits(y, "bf16"), want, [len(rows)], what="2^24 + 16 rows fwd")
+
+    # grad_x: grad_out [T, 128] -> grad_x [T, 32]
+    N, K = 128, 32
+    packed, scales = synth.packed_weights(d[3], d[4], 1, N, K)
+    gb = synth.normal_bf16(d[5], (4096, N), 0.1)
+    pt, st = gpu_weights(packed, scales)
+    g = tiled(gb)
+    gx = from_gpu_bits(mxq.mxfp4_grouped_mm_bwd_x(g, pt, st, ot)[torch.from_numpy(rows).to(dev())])
+    del g
+    want_b = oracle.grouped_mm_bwd_x(oracle.from_dtype_bits(gb[rows % 4096], "bf16"), packed, scales,
+                                     np.array([len(rows)], np.int32))
+    check_segments(oracle.from_dtype_bits(gx, "bf16"), want_b, [len(rows)], what="2^24 + 16 rows bwd_x")
+
+
 def test_autograd_function():
     E, T, N, K = 4, 400, 256, 512
     offs = np.array([100, 200, 300, 400], np.int32)
