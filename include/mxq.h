@@ -140,6 +140,27 @@ int mxfp4_grouped_mm_bwd_x(const void* grad_out, int64_t tokens, int64_t n,
                            const int8_t* packed, const uint8_t* scales, int64_t experts, int64_t k,
                            const int32_t* offs, void* grad_x, void* stream);
 
+/*
+ * mxfp4_grouped_mm_fwd_w4a4 -- the forward with the activations in MXFP4 too
+ * (W4A4; [MO] reports weight-and-activation FP4 as the variant that reaches
+ * the FP4 matrix units, where a dequantize-to-BF16 fallback does not).
+ * xq int8 [tokens, k/2] and xs E8M0 [tokens, k/32] are the activations as
+ * quantize_mxfp4 writes them ([MX] quantize_mxfp4, the floor rule); weights
+ * and offs as in mxfp4_grouped_mm_fwd.  Computes y[rows_e] = dq(xq)[rows_e] @
+ * dq(W_e)^T into y bf16 [tokens, n] on the block-scaled fp4 MFMA: products
+ * of codes and scales are exact, sums run in fp32, the output rounds
+ * nearest-even; rows past offs[experts-1] are written as zeros, offsets are
+ * clamped as in the forward.  A scale byte 0xFF makes the products it
+ * scales NaN.
+ * Needs k % 512 == 0 and k < 2^22, n % 8 == 0, one expert's packed weights
+ * below 2 GiB (n * k / 2 < 2^31), else MXQ_ERR_SHAPE; xq, xs, packed, scales
+ * and y 16-byte aligned, else MXQ_ERR_ALIGN; y must not overlap xq or xs
+ * (MXQ_ERR_ALIAS).  MXQ_ERR_HIP past 2^23 output tiles of 256 x 256.
+ */
+int mxfp4_grouped_mm_fwd_w4a4(const int8_t* xq, const uint8_t* xs, int64_t tokens, int64_t k,
+                              const int8_t* packed, const uint8_t* scales, int64_t experts, int64_t n,
+                              const int32_t* offs, void* y, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* mxq_status_string(int status);
 

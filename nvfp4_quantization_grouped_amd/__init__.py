@@ -14,6 +14,8 @@ from .ops import (
     dequantize_mxfp4,
     mxfp4_grouped_mm_bwd_x,
     mxfp4_grouped_mm_fwd,
+    mxfp4_grouped_mm_fwd_w4a4,
+    mxfp4_grouped_mm_fwd_w4a4_quantized,
     quantize_cache,
     quantize_cache_bwd,
     quantize_cache_forward,
@@ -24,5 +26,6 @@ __all__ = [
     "LIB_PATH", "EXPORTS", "MxqError", "lib",
     "MXFP4_BLOCK_SIZE", "CacheQuantization", "MXFP4GroupedMM",
     "dequantize_mxfp4", "mxfp4_grouped_mm_bwd_x", "mxfp4_grouped_mm_fwd",
+    "mxfp4_grouped_mm_fwd_w4a4", "mxfp4_grouped_mm_fwd_w4a4_quantized",
     "quantize_cache", "quantize_cache_bwd", "quantize_cache_forward", "quantize_mxfp4",
 ]

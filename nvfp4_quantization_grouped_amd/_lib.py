@@ -17,7 +17,7 @@ MXQ_FMT_FP8, MXQ_FMT_MXFP4, MXQ_FMT_NVFP4 = 0, 1, 2
 
 EXPORTS = (
     "quantize_mxfp4", "dequantize_mxfp4", "quantize_cache", "quantize_cache_bwd",
-    "mxfp4_grouped_mm_fwd", "mxfp4_grouped_mm_bwd_x", "mxq_status_string",
+    "mxfp4_grouped_mm_fwd", "mxfp4_grouped_mm_bwd_x", "mxfp4_grouped_mm_fwd_w4a4", "mxq_status_string",
 )
 
 _lib = None
@@ -30,6 +30,7 @@ _SIGS = {
     "quantize_cache_bwd": ([_vp, _vp, _int, _i64, _vp], _int),
     "mxfp4_grouped_mm_fwd": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp], _int),
     "mxfp4_grouped_mm_bwd_x": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp], _int),
+    "mxfp4_grouped_mm_fwd_w4a4": ([_vp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp], _int),
     "mxq_status_string": ([_int], ctypes.c_char_p),
 }
 

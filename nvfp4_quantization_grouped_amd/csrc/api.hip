@@ -104,6 +104,25 @@ int mxfp4_grouped_mm_bwd_x(const void* grad_out, int64_t tokens, int64_t n, cons
       mxq::launch_grouped_mm(true, grad_out, tokens, packed, scales, experts, n, k, offs, grad_x, (hipStream_t)stream));
 }
 
+int mxfp4_grouped_mm_fwd_w4a4(const int8_t* xq, const uint8_t* xs, int64_t tokens, int64_t k, const int8_t* packed,
+                              const uint8_t* scales, int64_t experts, int64_t n, const int32_t* offs, void* y,
+                              void* stream) {
+  if (tokens < 0 || k < 0 || n < 0 || experts < 0) return MXQ_ERR_SHAPE;
+  // whole 16-byte scale chunks per row; 32-bit buffer offsets into one expert's weights
+  if (k % 512 != 0 || n % 8 != 0 || k >= (int64_t(1) << 22) || n * (k / 2) >= (int64_t(1) << 31)) return MXQ_ERR_SHAPE;
+  if (tokens > 0 && n > 0 && (!y || (k > 0 && (!xq || !xs)) || (k > 0 && experts > 0 && (!packed || !scales || !offs))))
+    return MXQ_ERR_NULL;
+  if (((uintptr_t)xq & 15) || ((uintptr_t)xs & 15) || ((uintptr_t)packed & 15) || ((uintptr_t)scales & 15) ||
+      ((uintptr_t)y & 15))
+    return MXQ_ERR_ALIGN;
+  const int64_t ybytes = tokens * n * 2;
+  if (overlap(xq, tokens * (k / 2), y, ybytes) || overlap(xs, tokens * (k / 32), y, ybytes)) return MXQ_ERR_ALIAS;
+  if (tokens == 0 || n == 0) return MXQ_OK;
+  if (k == 0 || experts == 0) return from_hip(mxq::launch_zero(y, ybytes, (hipStream_t)stream));
+  return from_hip(
+      mxq::launch_grouped_mm_w4a4(xq, xs, tokens, packed, scales, experts, n, k, offs, y, (hipStream_t)stream));
+}
+
 const char* mxq_status_string(int s) {
   switch (s) {
     case MXQ_OK: return "ok";

@@ -32,6 +32,7 @@
 // range of row slots).  The backward remaps its workgroups the other way
 // (an XCD takes whole row slots with all their column tiles): its grad_out
 // tiles are the larger operand to re-fetch, and this measured 2-4% faster.
+#include <cstddef>
 #include <type_traits>
 
 #include "launch.hpp"
@@ -665,6 +666,190 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
                       col0 + wave * 64, ndim);
 }
 
+// ------------------------------------------------------ forward, W4A4
+// y[rows_e] = x_q[rows_e] @ W_e^T with the activations quantized to MXFP4 as
+// well (quantize_mxfp4: packed [T, K/2], E8M0 scales [T, K/32]), on gfx950's
+// block-scaled MFMA v_mfma_scale_f32_32x32x64_f8f6f4 with both operands fp4
+// e2m1.  Its operand layout (pinned by an in-bounds probe against a float64
+// reference, to fp32 rounding): lane l carries row (or column) l % 32 and
+// the 32 consecutive k of block l / 32 of the 64-k sub-step, two codes per
+// byte with the even k in the low nibble -- exactly one stored row segment
+// and its E8M0 block -- and byte 0 of its scale register scales that block
+// (a 0xFF scale gives NaN).  So no code is decoded here: both operands go
+// from global memory through LDS into the MFMA as stored.  Products of two
+// e2m1 codes and two power-of-two scales are exact, sums run in fp32, the
+// output rounds to bf16 nearest-even.
+//
+// Workgroup: 8 waves, a 256 x 256 output tile; wave (wm, wn) = (wave / 4,
+// wave % 4) owns rows [128 wm, +128) and columns [64 wn, +64), 4 x 2 MFMA
+// tiles computed transposed (weight fragment first, as in the bf16 kernels,
+// so the LDS-staged epilogue is shared).  The reduction runs in stages of
+// 128 k (64 bytes of each row), 2 MFMA sub-steps each, through a ring of 4
+// LDS stages filled by buffer->LDS DMA three stages ahead; a stage row's four
+// 16-byte chunks are XOR-swizzled by (row >> 2) & 3, so the 16 rows one
+// fragment read touches per LDS cycle hit 16 distinct bank groups.  Scales
+// come 16 bytes (512 k, 4 stages) per row at a time into a double buffer.
+// Needs K % 512 == 0 (16-byte aligned scale rows).
+constexpr int kW4BM = 256, kW4BN = 256, kW4Threads = 512, kW4Stages = 4;
+
+struct W4Smem {
+  uint8_t a[kW4Stages][kW4BM * 64];   // activation codes: 256 rows x 64 bytes (128 k) per stage
+  uint8_t b[kW4Stages][kW4BN * 64];   // weight codes: 256 columns x 64 bytes
+  uint8_t sa[2][kW4BM * 16];          // activation scales: 16 bytes (512 k) per row
+  uint8_t sb[2][kW4BN * 16];          // weight scales
+};
+
+typedef int v8i32_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x16_t mfma_w4(const u32x4_t& w, const u32x4_t& x, uint32_t sw, uint32_t sx,
+                                            const f32x16_t& c) {
+  const v8i32_t a = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
+  const v8i32_t b = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, (int)sw, 0, (int)sx);
+}
+
+__global__ void __launch_bounds__(kW4Threads, 1)
+k_grouped_mm_fwd_w4a4(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+                      const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
+                      const int32_t* __restrict__ offs, int experts, int64_t tokens, int64_t ndim, int64_t kdim,
+                      uint8_t* __restrict__ out, int gx) {
+  constexpr int BM = kW4BM, BN = kW4BN, MT = 4, NT = 2, S = kW4Stages, kThreads = kW4Threads;
+  const int64_t col0 = (int64_t)(blockIdx.x % gx) * BN;
+  TileTable<BM> tt;
+  tt.build(offs, experts, tokens);
+  const TileInfo ti = tt.lookup((int)(blockIdx.x / gx));
+  if (ti.expert == -2) return;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 2, wn = wave & 3, h = lane >> 5, r = lane & 31;
+
+  if (ti.expert == -1) {
+    for (int i = threadIdx.x; i < BM * BN / 8; i += kThreads) {
+      const int rr = i / (BN / 8), c = (i % (BN / 8)) * 8;
+      const int64_t gr = ti.row0 + rr, gc = col0 + c;
+      if (gr < ti.row_end && gc < ndim) {
+        unsigned short* dst = reinterpret_cast<unsigned short*>(out + (gr * ndim + gc) * 2);
+        for (int q = 0; q < 8 && gc + q < ndim; ++q) dst[q] = 0;
+      }
+    }
+    return;
+  }
+
+  __shared__ __attribute__((aligned(1024))) W4Smem sm;
+
+  // buffers over this tile's activation rows and weight columns (reads past
+  // the expert's rows or past n return zeros); ranges fit 31 bits (the
+  // launcher checks one expert's packed weights, and K < 2^22)
+  const int64_t prow = kdim / 2, srow = kdim / 32;
+  const int64_t nrows = min(ti.row_end - ti.row0, (int64_t)BM);
+  const __amdgpu_buffer_rsrc_t rs_a = dma_rsrc(xq + ti.row0 * prow, nrows * prow);
+  const __amdgpu_buffer_rsrc_t rs_sa = dma_rsrc(xs + ti.row0 * srow, nrows * srow);
+  const __amdgpu_buffer_rsrc_t rs_b = dma_rsrc(packed_e_of(packed, ti.expert, ndim, kdim) + col0 * prow, (ndim - col0) * prow);
+  const __amdgpu_buffer_rsrc_t rs_sb =
+      dma_rsrc(scales + ((int64_t)ti.expert * ndim + col0) * srow, (ndim - col0) * srow);
+  // code transfers: op q (16 rows) of a stage, wave w moves ops 2w and 2w+1
+  // of both operands; lane l -> row 16q + l/4, LDS chunk l%4 <- global chunk
+  // (l%4) ^ ((row >> 2) & 3)
+  uint32_t c_off[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 16 * (2 * wave + j) + (lane >> 2);
+    c_off[j] = (uint32_t)(row * prow + 16 * ((lane & 3) ^ ((row >> 2) & 3)));
+  }
+  // scale transfers: wave w < 4 moves activation rows 64w .. 64w+63, wave
+  // w >= 4 weight columns 64(w-4) ..; 16 bytes per lane
+  const bool s_is_a = wave < 4;
+  const uint32_t s_off = (uint32_t)((64 * (wave & 3) + lane) * srow);
+  auto issue_codes = [&](int st, int stage, int j) {   // j = 0, 1: the wave's two ops of one operand pair
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_void_t*)(sm.a[st] + 1024 * (2 * wave + j)), 16, c_off[j],
+                                             stage * 64, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void_t*)(sm.b[st] + 1024 * (2 * wave + j)), 16, c_off[j],
+                                             stage * 64, 0, 0);
+  };
+  auto issue_scales = [&](int chunk) {
+    uint8_t* dst = (s_is_a ? sm.sa[chunk & 1] : sm.sb[chunk & 1]) + 1024 * (wave & 3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_is_a ? rs_sa : rs_sb, (lds_void_t*)dst, 16, s_off, 16 * chunk, 0, 0);
+  };
+
+  f32x16_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x16_t{};
+
+  const int nst = (int)(kdim / 128);      // >= 4 (K % 512 == 0)
+  const int last = nst - 1, last_chunk = (nst - 1) >> 2;
+  issue_scales(0);
+#pragma unroll
+  for (int t = 0; t < S - 1; ++t) {
+    issue_codes(t, t, 0);
+    issue_codes(t, t, 1);
+  }
+  // stage 0 and scale chunk 0 have landed once only stages 1, 2 (4 ops each) may be in flight
+  wait_vmcnt_barrier<8>();
+
+  // fragment addresses: rows 128 wm + 32 i + r share (row >> 2) & 3 = (r >> 2) & 3
+  const int swz = (r >> 2) & 3;
+  const int a_row = (128 * wm + r) * 64, b_row = (64 * wn + r) * 64;
+  const int sa_row = (128 * wm + r) * 16, sb_row = (64 * wn + r) * 16;
+  for (int s = 0; s < nst; ++s) {
+    __builtin_amdgcn_sched_barrier(0);
+    const int st = s & (S - 1);
+    const bool chunk_start = (s & 3) == 0;
+    if (chunk_start) issue_scales(min((s >> 2) + 1, last_chunk));
+    const bool refill = s + S - 1 <= last;
+    const int nstg = (s + S - 1) & (S - 1);
+    // this stage's scale dwords: blocks 4 (s & 3) .. +3 of the chunk, in the
+    // order (sub-step 0, half 0), (0, 1), (1, 0), (1, 1)
+    const uint8_t* sa_c = sm.sa[(s >> 2) & 1] + 4 * (s & 3);
+    const uint8_t* sb_c = sm.sb[(s >> 2) & 1] + 4 * (s & 3);
+    uint32_t scx[MT], scw[NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) scx[i] = *reinterpret_cast<const uint32_t*>(sa_c + sa_row + i * 32 * 16);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) scw[j] = *reinterpret_cast<const uint32_t*>(sb_c + sb_row + j * 32 * 16);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int off = 16 * ((2 * kk + h) ^ swz);
+      u32x4_t fx[MT], fw[NT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) fx[i] = *reinterpret_cast<const u32x4_t*>(sm.a[st] + a_row + i * 32 * 64 + off);
+#pragma unroll
+      for (int j = 0; j < NT; ++j) fw[j] = *reinterpret_cast<const u32x4_t*>(sm.b[st] + b_row + j * 32 * 64 + off);
+      if (refill) issue_codes(nstg, s + S - 1, kk);
+      const int sh = 8 * (2 * kk + h);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = mfma_w4(fw[j], fx[i], (scw[j] >> sh) & 0xFF, (scx[i] >> sh) & 0xFF, acc[i][j]);
+    }
+    // stage s+1 (and its scale chunk) have landed once only the transfers
+    // issued after stage s+1's may be in flight: stages s+2 and s+3 (4 ops
+    // each, when they exist) and the scale chunks of this stage and the last
+    const bool c_prev = s >= 1 && ((s - 1) & 3) == 0;
+    const int pend = (s + 2 <= last ? 4 : 0) + (refill ? 4 : 0) + (chunk_start ? 1 : 0) + (c_prev ? 1 : 0);
+    switch (pend) {
+      case 10: wait_vmcnt_barrier<10>(); break;
+      case 9: wait_vmcnt_barrier<9>(); break;
+      case 8: wait_vmcnt_barrier<8>(); break;
+      case 6: wait_vmcnt_barrier<6>(); break;
+      case 5: wait_vmcnt_barrier<5>(); break;
+      case 4: wait_vmcnt_barrier<4>(); break;
+      case 2: wait_vmcnt_barrier<2>(); break;
+      case 1: wait_vmcnt_barrier<1>(); break;
+      default: wait_vmcnt_barrier<0>(); break;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // the last stage's barrier has retired every read of the ring; drain the
+  // clamped scale transfer (it lands outside the epilogue block)
+  __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
+  static_assert(offsetof(W4Smem, sa) >= (size_t)8 * 128 * 128, "epilogue block fits in front of the scales");
+  store_block_lds<MT>(reinterpret_cast<uint8_t*>(&sm) + wave * 128 * 128, acc, lane, out, ndim, ti.row0 + 128 * wm,
+                      ti.row_end, col0 + wn * 64, ndim);
+}
+
 // ----------------------------------------------------------------- backward
 // grad_x = grad_out @ W_e.  Tile: 256 token rows x 256 output columns (k),
 // reduction over n in steps of 64; 8 waves, one workgroup per CU.  Wave
@@ -977,6 +1162,17 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
                        (int)gx);
     return hipGetLastError();
   }
+}
+
+hipError_t launch_grouped_mm_w4a4(const void* xq, const uint8_t* xs, int64_t tokens, const int8_t* packed,
+                                  const uint8_t* scales, int64_t experts, int64_t n, int64_t k, const int32_t* offs,
+                                  void* out, hipStream_t st) {
+  const int64_t gx = (n + kW4BN - 1) / kW4BN;
+  const int64_t gy = (tokens + kW4BM - 1) / kW4BM + experts;
+  if (!grid_fits(gx * gy, kW4Threads)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(k_grouped_mm_fwd_w4a4, dim3((unsigned)(gx * gy)), dim3(kW4Threads), 0, st, (const uint8_t*)xq, xs,
+                     (const uint8_t*)packed, scales, offs, (int)experts, tokens, n, k, (uint8_t*)out, (int)gx);
+  return hipGetLastError();
 }
 
 }  // namespace mxq

@@ -20,5 +20,9 @@ hipError_t launch_zero(void* dst, int64_t bytes, hipStream_t st);
 hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8_t* packed, const uint8_t* scales,
                              int64_t experts, int64_t wn_dim, int64_t wk_dim, const int32_t* offs, void* out,
                              hipStream_t st);
+// out[T, N] = dq(xq)[T, K] dq(W_e)^T, both operands MXFP4 (K % 512 == 0).
+hipError_t launch_grouped_mm_w4a4(const void* xq, const uint8_t* xs, int64_t tokens, const int8_t* packed,
+                                  const uint8_t* scales, int64_t experts, int64_t n, int64_t k, const int32_t* offs,
+                                  void* out, hipStream_t st);
 
 }  // namespace mxq

@@ -184,6 +184,42 @@ def mxfp4_grouped_mm_bwd_x(grad_out, packed, scales, offs):
     return gx
 
 
+def mxfp4_grouped_mm_fwd_w4a4_quantized(xq, xs, packed, scales, offs):
+    """y [T, N] = dq(xq)[rows_e] @ dq(W_e)^T per expert segment, activations
+    already in MXFP4 (int8 [T, K/2] and E8M0 [T, K/32] as quantize_mxfp4
+    returns them); K % 512 == 0.  bf16 output."""
+    _need_cuda(xq, xs, packed, scales, offs)
+    xs8, s = _as_u8(xs), _as_u8(scales)
+    if offs.dtype != torch.int32:
+        raise TypeError("mxfp4_grouped_mm_fwd_w4a4: offs must be int32")
+    if packed.dim() != 3 or s.dim() != 3 or offs.dim() != 1 or xq.dim() != 2 or xs8.dim() != 2:
+        raise ValueError("mxfp4_grouped_mm_fwd_w4a4: xq [T, K/2], xs [T, K/32], packed [E, N, K/2], "
+                         "scales [E, N, K/32], offs [E]")
+    E, N, K2 = packed.shape
+    T = xq.shape[0]
+    if (tuple(s.shape) != (E, N, K2 * 2 // 32) or offs.shape[0] != E or xq.shape[1] != K2
+            or tuple(xs8.shape) != (T, K2 * 2 // 32)):
+        raise ValueError("mxfp4_grouped_mm_fwd_w4a4: inconsistent shapes")
+    xq, xs8, p, s, o = xq.contiguous(), xs8.contiguous(), packed.contiguous(), s.contiguous(), offs.contiguous()
+    y = torch.empty(T, N, dtype=torch.bfloat16, device=xq.device)
+    with torch.cuda.device(xq.device):
+        st = _lib.lib().mxfp4_grouped_mm_fwd_w4a4(_ptr(xq), _ptr(xs8), T, K2 * 2, _ptr(p), _ptr(s), E, N, _ptr(o),
+                                                  _ptr(y), _stream(xq.device))
+    _lib.check(st, "mxfp4_grouped_mm_fwd_w4a4")
+    return y
+
+
+def mxfp4_grouped_mm_fwd_w4a4(x, packed, scales, offs):
+    """W4A4 forward: quantize_mxfp4(x) (bf16 x [T, K], per 32-block E8M0
+    scales by the floor rule), then the grouped GEMM of the two MXFP4
+    operands on the block-scaled fp4 MFMA.  K % 512 == 0."""
+    _need_cuda(x)
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise TypeError("mxfp4_grouped_mm_fwd_w4a4: x must be bfloat16 [tokens, K]")
+    xq, xs = quantize_mxfp4(x)
+    return mxfp4_grouped_mm_fwd_w4a4_quantized(xq, xs, packed, scales, offs)
+
+
 class MXFP4GroupedMM(torch.autograd.Function):
     """Grouped GEMM over mxfp4-packed frozen expert weights.  Saves only the
     packed weights, scales and offsets; the backward dequantizes again inside

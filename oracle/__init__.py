@@ -42,7 +42,8 @@ from .formats import (
 )
 from .mxfp4 import quantize_mxfp4, dequantize_mxfp4, floor_scale_exponent
 from .cache import power_of_two_ceiling, cache_scale, quantize_cache, quantize_cache_backward
-from .grouped_mm import dequantize_expert_weights, grouped_mm_fwd, grouped_mm_bwd_x, grouped_mm_rows, segments
+from .grouped_mm import (dequantize_expert_weights, grouped_mm_fwd, grouped_mm_bwd_x, grouped_mm_rows, segments,
+                         w4a4_activations, grouped_mm_fwd_w4a4)
 
 __all__ = [
     "E2M1_TABLE", "E2M1_MIDPOINTS", "MXFP4_BLOCK_SIZE", "E4M3_MAX",
@@ -51,4 +52,5 @@ __all__ = [
     "quantize_mxfp4", "dequantize_mxfp4", "floor_scale_exponent",
     "power_of_two_ceiling", "cache_scale", "quantize_cache", "quantize_cache_backward",
     "dequantize_expert_weights", "grouped_mm_fwd", "grouped_mm_bwd_x", "grouped_mm_rows", "segments",
+    "w4a4_activations", "grouped_mm_fwd_w4a4",
 ]

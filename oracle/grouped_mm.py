@@ -15,7 +15,7 @@ Test infrastructure only (see ``oracle/__init__.py``).  float64 throughout.
 
 import numpy as np
 
-from .mxfp4 import dequantize_mxfp4_values
+from .mxfp4 import dequantize_mxfp4_values, quantize_mxfp4
 
 
 def segments(offs, tokens):
@@ -85,6 +85,28 @@ def grouped_mm_bwd_x(grad_out, packed, scales, offs, rows=None):
         w = dequantize_expert_weights(packed, scales, e)           # [N, K]
         gx[sel] = g[sel] @ w
     return gx
+
+
+def w4a4_activations(x):
+    """Exact float64 values of activations x [T, K] after MXFP4 quantization
+    by ``quantize_mxfp4`` (per token row, 32-blocks along K, floor scale rule).
+
+    Reading: "NVIDIA Model Optimizer: from mtq.quantize to a 4.95-bit
+    DeepSeek-R1" (the section on weight-only 4-bit against W4A4) names the
+    weight-and-activation FP4 form as the one that runs on the FP4 matrix
+    units, and "nemo_automodel.components.quantization.mxfp4" has one MXFP4
+    quantizer, ``quantize_mxfp4``; the activations of the W4A4 forward are
+    taken to be quantized by it.  Each row is independent, so a subset of
+    rows can be quantized on its own."""
+    xq, xs = quantize_mxfp4(np.asarray(x, dtype=np.float64))
+    return dequantize_mxfp4_values(xq, xs)
+
+
+def grouped_mm_fwd_w4a4(x, packed, scales, offs, rows=None):
+    """W4A4 forward: y[rows_e] = q(x)[rows_e] @ W_e^T, with q the MXFP4
+    round trip of ``w4a4_activations``, then ``grouped_mm_fwd`` on those
+    exact values (float64).  ``rows`` as in ``grouped_mm_fwd``."""
+    return grouped_mm_fwd(w4a4_activations(x), packed, scales, offs, rows=rows)
 
 
 def grouped_mm_rows(rows, packed, scales, offs, x_rows=None, g_rows=None):

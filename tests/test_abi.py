@@ -99,6 +99,31 @@ def test_grouped_mm_validation(L):
     assert b(FAKE, 1, 1 << 16, FAKE * 2, FAKE * 3, 2, 1 << 16, FAKE * 4, FAKE * 5, None) == -2
 
 
+def test_grouped_mm_w4a4_validation(L):
+    f = L.mxfp4_grouped_mm_fwd_w4a4
+    # (xq, xs, tokens, k, packed, scales, experts, n, offs, y, stream)
+    ok = (FAKE, FAKE * 2, 16, 512, FAKE * 3, FAKE * 4, 2, 64, FAKE * 5, FAKE * 6, None)
+    def call(**kw):
+        names = ("xq", "xs", "tokens", "k", "packed", "scales", "experts", "n", "offs", "y", "stream")
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return f(*[args[n] for n in names])
+    assert call(k=256) == -2                      # whole 512-k scale chunks
+    assert call(k=544) == -2
+    assert call(n=60) == -2                       # n % 8
+    assert call(tokens=-1) == -2
+    assert call(k=1 << 22) == -2                  # 32-bit offsets
+    assert call(k=1 << 16, n=1 << 16) == -2       # one expert's packed weights reach 2 GiB
+    assert call(xq=None) == -1
+    assert call(scales=None) == -1
+    assert call(xs=FAKE * 2 + 4) == -6            # every operand 16-byte aligned
+    assert call(scales=FAKE * 4 + 8) == -6
+    assert call(y=FAKE * 6 + 2) == -6
+    assert call(y=FAKE + 16) == -7                # y overlaps xq
+    assert call(tokens=0) == 0                    # nothing to do
+    assert call(n=0) == 0
+
+
 def test_ops_reject_cpu_tensors():
     import torch
     with pytest.raises(ValueError):

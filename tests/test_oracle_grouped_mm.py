@@ -136,3 +136,73 @@ def test_offsets_preconditions():
         oracle.grouped_mm_fwd(x, packed, scales, np.array([4, 3], np.int32))
     with pytest.raises(ValueError):
         oracle.grouped_mm_fwd(x, packed, scales, np.array([4, 7], np.int32))
+
+
+# ---- W4A4 forward (activations through quantize_mxfp4 as well)
+
+_GRID = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]   # e2m1 magnitudes by code
+
+
+def _brute_mxfp4_value(v, e):
+    """Nearest e2m1 grid value of v / 2^e, ties to the even code, times 2^e,
+    by search over the grid."""
+    q = abs(v) / 2.0 ** e
+    best = min(range(8), key=lambda c: (abs(q - _GRID[c]), c % 2))
+    return (-1.0 if v < 0 else 1.0) * _GRID[best] * 2.0 ** e
+
+
+def _brute_floor_exponent(amax):
+    if amax == 0:
+        return -127
+    e = -200
+    while 2.0 ** (e + 1) <= amax:   # largest e with 2^e <= amax
+        e += 1
+    return max(-127, min(127, e - 2))
+
+
+def test_w4a4_matches_brute_force():
+    """Per-element scalar quantization (exponent by search, nearest grid value
+    with ties to the even code) and an explicit triple loop, on 2 experts."""
+    g = np.random.default_rng(5)
+    E, T, N, K = 2, 5, 3, 64
+    packed, scales = rand_weights(g, E, N, K)
+    x = g.standard_normal((T, K)) * np.repeat(2.0 ** g.integers(-6, 7, size=(T, K // 32)), 32, axis=1)
+    # planted ties on the e2m1 grid (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 times the block scale),
+    # filling the whole block, so its maximum 5 * 2^-3 fixes the scale exponent at -3
+    x[0, :32] = np.tile([4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], 4) * 2.0 ** -3
+    x[1, 32:] = 0.0                                          # an all-zero block
+    x[2, 40] = 7.5 * 2.0 ** 4                                # saturating block maximum
+    offs = np.array([2, 5], np.int32)
+    y = oracle.grouped_mm_fwd_w4a4(x, packed, scales, offs)
+    for t in range(T):
+        e_t = 0 if t < 2 else 1
+        xv = []
+        for b in range(K // 32):
+            blk = x[t, 32 * b:32 * b + 32]
+            e = _brute_floor_exponent(max(abs(v) for v in blk))
+            xv += [_brute_mxfp4_value(v, e) for v in blk]
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                byte = int(packed[e_t, n, k // 2]) & 0xFF
+                nib = byte & 0xF if k % 2 == 0 else byte >> 4
+                w = (-1.0 if nib & 8 else 1.0) * _GRID[nib & 7] * 2.0 ** (int(scales[e_t, n, k // 32]) - 127)
+                acc += xv[k] * w
+            assert abs(y[t, n] - acc) <= 1e-12 * max(1.0, abs(acc)), (t, n, y[t, n], acc)
+
+
+def test_w4a4_on_grid_values_is_the_plain_forward():
+    """Activations already on the MXFP4 grid (one round trip) are fixed points
+    of the quantizer, so the W4A4 forward equals the plain forward exactly;
+    off-grid activations do not."""
+    g = np.random.default_rng(6)
+    E, T, N, K = 3, 40, 16, 128
+    packed, scales = rand_weights(g, E, N, K)
+    offs = np.array([10, 10, 33], np.int32)
+    x0 = g.standard_normal((T, K))
+    xg = oracle.w4a4_activations(x0)
+    assert np.array_equal(oracle.w4a4_activations(xg), xg)
+    assert np.array_equal(oracle.grouped_mm_fwd_w4a4(xg, packed, scales, offs),
+                          oracle.grouped_mm_fwd(xg, packed, scales, offs))
+    assert not np.allclose(oracle.grouped_mm_fwd_w4a4(x0, packed, scales, offs),
+                           oracle.grouped_mm_fwd(x0, packed, scales, offs))
