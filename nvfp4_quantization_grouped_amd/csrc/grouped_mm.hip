@@ -776,8 +776,7 @@ k_grouped_mm_fwd_w4a4(const uint8_t* __restrict__ xq, const uint8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x16_t{};
 
-  const int nst = (int)(kdim / 128);      // >= 4 (K % 512 == 0)
-  const int last = nst - 1, last_chunk = (nst - 1) >> 2;
+  const int last = (int)(kdim / 128) - 1, last_chunk = last >> 2;
   issue_scales(0);
 #pragma unroll
   for (int t = 0; t < S - 1; ++t) {
@@ -791,60 +790,95 @@ k_grouped_mm_fwd_w4a4(const uint8_t* __restrict__ xq, const uint8_t* __restrict_
   const int swz = (r >> 2) & 3;
   const int a_row = (128 * wm + r) * 64, b_row = (64 * wn + r) * 64;
   const int sa_row = (128 * wm + r) * 16, sb_row = (64 * wn + r) * 16;
-  for (int s = 0; s < nst; ++s) {
+  struct Half {                  // one sub-step's fragments
+    u32x4_t x[MT], w[NT];
+  };
+  struct Scl {                   // a stage's scale dwords: blocks of (sub-step 0, half 0), (0, 1), (1, 0), (1, 1)
+    uint32_t x[MT], w[NT];
+  };
+  auto read_half = [&](Half& f, int s, int kk) {
+    const int st = s & (S - 1), off = 16 * ((2 * kk + h) ^ swz);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) f.x[i] = *reinterpret_cast<const u32x4_t*>(sm.a[st] + a_row + i * 32 * 64 + off);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) f.w[j] = *reinterpret_cast<const u32x4_t*>(sm.b[st] + b_row + j * 32 * 64 + off);
+  };
+  auto read_scales = [&](Scl& c, int s) {
+    const uint8_t* sa_c = sm.sa[(s >> 2) & 1] + 4 * (s & 3);
+    const uint8_t* sb_c = sm.sb[(s >> 2) & 1] + 4 * (s & 3);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) c.x[i] = *reinterpret_cast<const uint32_t*>(sa_c + sa_row + i * 32 * 16);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) c.w[j] = *reinterpret_cast<const uint32_t*>(sb_c + sb_row + j * 32 * 16);
+  };
+  auto mfmas = [&](const Half& f, const Scl& c, int kk) {
+    const int sh = 8 * (2 * kk + h);
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        acc[i][j] = mfma_w4(f.w[j], f.x[i], (c.w[j] >> sh) & 0xFF, (c.x[i] >> sh) & 0xFF, acc[i][j]);
+  };
+  // Stage s, entered with its sub-step 0 fragments and its scales in
+  // registers (k0, sc): read its sub-step 1 fragments; refill ring slot
+  // (s + 3) % 4 -- stage s - 1's, whose reads every wave finished before the
+  // barrier in the middle of stage s - 1 -- with stage s + 3; sub-step 0's
+  // MFMAs; wait for stage s + 1 and barrier; read stage s + 1's sub-step 0
+  // fragments and scales into (nk0, nsc); sub-step 1's MFMAs.  Each batch of
+  // reads is covered by 8 MFMAs per wave, and the MFMA pipe keeps sub-step
+  // 1's work across the barrier (with one workgroup per CU, a barrier at the
+  // end of the stage drained the pipe every stage).  Stage s's reads all
+  // precede the barrier in its middle, and its slot is refilled only in
+  // stage s + 1.
+  auto stage = [&](const Half& k0, const Scl& sc, Half& nk0, Scl& nsc, int s) {
     __builtin_amdgcn_sched_barrier(0);
-    const int st = s & (S - 1);
+    Half k1;
+    read_half(k1, s, 1);
     const bool chunk_start = (s & 3) == 0;
     if (chunk_start) issue_scales(min((s >> 2) + 1, last_chunk));
     const bool refill = s + S - 1 <= last;
     const int nstg = (s + S - 1) & (S - 1);
-    // this stage's scale dwords: blocks 4 (s & 3) .. +3 of the chunk, in the
-    // order (sub-step 0, half 0), (0, 1), (1, 0), (1, 1)
-    const uint8_t* sa_c = sm.sa[(s >> 2) & 1] + 4 * (s & 3);
-    const uint8_t* sb_c = sm.sb[(s >> 2) & 1] + 4 * (s & 3);
-    uint32_t scx[MT], scw[NT];
-#pragma unroll
-    for (int i = 0; i < MT; ++i) scx[i] = *reinterpret_cast<const uint32_t*>(sa_c + sa_row + i * 32 * 16);
-#pragma unroll
-    for (int j = 0; j < NT; ++j) scw[j] = *reinterpret_cast<const uint32_t*>(sb_c + sb_row + j * 32 * 16);
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const int off = 16 * ((2 * kk + h) ^ swz);
-      u32x4_t fx[MT], fw[NT];
-#pragma unroll
-      for (int i = 0; i < MT; ++i) fx[i] = *reinterpret_cast<const u32x4_t*>(sm.a[st] + a_row + i * 32 * 64 + off);
-#pragma unroll
-      for (int j = 0; j < NT; ++j) fw[j] = *reinterpret_cast<const u32x4_t*>(sm.b[st] + b_row + j * 32 * 64 + off);
-      if (refill) issue_codes(nstg, s + S - 1, kk);
-      const int sh = 8 * (2 * kk + h);
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NT; ++j)
-          acc[i][j] = mfma_w4(fw[j], fx[i], (scw[j] >> sh) & 0xFF, (scx[i] >> sh) & 0xFF, acc[i][j]);
+    if (refill) issue_codes(nstg, s + S - 1, 0);
+    mfmas(k0, sc, 0);
+    if (refill) issue_codes(nstg, s + S - 1, 1);
+    if (s + 1 <= last) {
+      // stage s+1 (and its scale chunk) have landed once only the transfers
+      // issued after stage s+1's may be in flight: stages s+2 and s+3 (4 ops
+      // each, when they exist) and the scale chunks issued at stages s-1, s
+      const bool c_prev = s >= 1 && ((s - 1) & 3) == 0;
+      const int pend = (s + 2 <= last ? 4 : 0) + (refill ? 4 : 0) + (chunk_start ? 1 : 0) + (c_prev ? 1 : 0);
+      __builtin_amdgcn_sched_barrier(0);
+      switch (pend) {
+        case 9: wait_vmcnt_barrier<9>(); break;
+        case 8: wait_vmcnt_barrier<8>(); break;
+        case 5: wait_vmcnt_barrier<5>(); break;
+        case 4: wait_vmcnt_barrier<4>(); break;
+        case 1: wait_vmcnt_barrier<1>(); break;
+        default: wait_vmcnt_barrier<0>(); break;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      read_half(nk0, s + 1, 0);
+      read_scales(nsc, s + 1);
     }
-    // stage s+1 (and its scale chunk) have landed once only the transfers
-    // issued after stage s+1's may be in flight: stages s+2 and s+3 (4 ops
-    // each, when they exist) and the scale chunks of this stage and the last
-    const bool c_prev = s >= 1 && ((s - 1) & 3) == 0;
-    const int pend = (s + 2 <= last ? 4 : 0) + (refill ? 4 : 0) + (chunk_start ? 1 : 0) + (c_prev ? 1 : 0);
-    switch (pend) {
-      case 10: wait_vmcnt_barrier<10>(); break;
-      case 9: wait_vmcnt_barrier<9>(); break;
-      case 8: wait_vmcnt_barrier<8>(); break;
-      case 6: wait_vmcnt_barrier<6>(); break;
-      case 5: wait_vmcnt_barrier<5>(); break;
-      case 4: wait_vmcnt_barrier<4>(); break;
-      case 2: wait_vmcnt_barrier<2>(); break;
-      case 1: wait_vmcnt_barrier<1>(); break;
-      default: wait_vmcnt_barrier<0>(); break;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
+    mfmas(k1, sc, 1);
+  };
 
-  // the last stage's barrier has retired every read of the ring; drain the
-  // clamped scale transfer (it lands outside the epilogue block)
+  const int nst = (int)(kdim / 128);      // >= 4 and even (K % 512 == 0)
+  Half h0, h1;
+  Scl c0, c1;
+  read_half(h0, 0, 0);
+  read_scales(c0, 0);
+  for (int s = 0; s < nst; s += 2) {
+    stage(h0, c0, h1, c1, s);
+    stage(h1, c1, h0, c0, s + 1);
+  }
+  // every wave's fragment reads of the ring are done before any wave stages
+  // its output there (no code transfer is pending: the last one, stage
+  // last's, was waited for in the middle of stage last - 1); drain the
+  // clamped scale transfer too (it lands outside the epilogue block)
   __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("s_barrier" ::: "memory");
   static_assert(offsetof(W4Smem, sa) >= (size_t)8 * 128 * 128, "epilogue block fits in front of the scales");
   store_block_lds<MT>(reinterpret_cast<uint8_t*>(&sm) + wave * 128 * 128, acc, lane, out, ndim, ti.row0 + 128 * wm,
                       ti.row_end, col0 + wn * 64, ndim);
