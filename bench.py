@@ -35,6 +35,7 @@ import time
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+MFMA_FP4_PEAK_TFLOPS = 10100.0   # MI355X dense fp4 (MXFP4) MFMA
 METRIC = "quant/dequant GB/s (% HBM peak); MXFP4 grouped-GEMM TFLOP/s (% MFMA peak)"
 
 
@@ -49,8 +50,10 @@ def parse():
 
 
 class Leg:
-    def __init__(self, name, kernel, kind, work, fn, reps=1):
+    def __init__(self, name, kernel, kind, work, fn, reps=1, peak=None):
         self.name, self.kernel, self.kind, self.work, self.fn, self.reps = name, kernel, kind, work, fn, reps
+        # the roof this leg's rate is a fraction of (TFLOP/s or GB/s)
+        self.peak = peak or (MFMA_BF16_PEAK_TFLOPS if kind == "flop" else HBM_PEAK_GBPS)
         self.ms = 0.0   # summed event time over the timed steps
 
     def run(self, step):
@@ -95,7 +98,7 @@ def main():
 
     # ---------------- routed-expert layer (gate/up + down, fwd + grad_x)
     moe = None
-    if wanted("moe"):
+    if wanted("moe") or wanted("w4a4"):
         moe = synth.moe_layer(seed=0)
         T = int(moe["offs"][-1])
         E, H, I2, I = 32, 7168, 4096, 2048
@@ -125,6 +128,34 @@ def main():
             Leg("moe.down.bwd_x", "k_grouped_mm_bwd", "flop", 2.0 * moe_rows * H * I, bwd(dn_g, dn_p, dn_s, H, I, dn_gx)),
             Leg("moe.gate_up.bwd_x", "k_grouped_mm_bwd", "flop", 2.0 * moe_rows * I2 * H, bwd(gu_g, gu_p, gu_s, I2, H, gu_gx)),
         ]
+
+        # the same forwards as W4A4: the activations quantized to MXFP4
+        # (quantize_mxfp4), then the block-scaled fp4 MFMA GEMM
+        if wanted("w4a4"):
+            gu_xq = torch.empty(T, H // 2, dtype=torch.int8, device=dev)
+            gu_xs = torch.empty(T, H // 32, dtype=torch.uint8, device=dev)
+            dn_xq = torch.empty(T, I // 2, dtype=torch.int8, device=dev)
+            dn_xs = torch.empty(T, I // 32, dtype=torch.uint8, device=dev)
+
+            def quant(a, k, xq, xs):
+                return lambda i: check(L.quantize_mxfp4(a.data_ptr(), mxq._lib.MXQ_BF16, T, k, xq.data_ptr(),
+                                                        xs.data_ptr(), sp), "quantize x")
+
+            def w4(xq, xs, p, s, n, k, y):
+                return lambda i: check(L.mxfp4_grouped_mm_fwd_w4a4(xq.data_ptr(), xs.data_ptr(), T, k, p.data_ptr(),
+                                                                   s.data_ptr(), E, n, offs.data_ptr(), y.data_ptr(),
+                                                                   sp), "w4a4 fwd")
+
+            legs += [
+                Leg("w4a4.gate_up.quantize_x", "k_quantize_mxfp4<bf16>", "byte", T * H * (2 + 0.5 + 1 / 32),
+                    quant(x_routed, H, gu_xq, gu_xs)),
+                Leg("w4a4.gate_up.fwd", "k_grouped_mm_fwd_w4a4", "flop", 2.0 * moe_rows * I2 * H,
+                    w4(gu_xq, gu_xs, gu_p, gu_s, I2, H, gu_y), peak=MFMA_FP4_PEAK_TFLOPS),
+                Leg("w4a4.down.quantize_x", "k_quantize_mxfp4<bf16>", "byte", T * I * (2 + 0.5 + 1 / 32),
+                    quant(h, I, dn_xq, dn_xs)),
+                Leg("w4a4.down.fwd", "k_grouped_mm_fwd_w4a4", "flop", 2.0 * moe_rows * H * I,
+                    w4(dn_xq, dn_xs, dn_p, dn_s, H, I, dn_y), peak=MFMA_FP4_PEAK_TFLOPS),
+            ]
 
     # ---------------- 8-expert grouped GEMM forward (4 rotating buffer sets > 256 MB)
     if wanted("e8"):
@@ -239,7 +270,9 @@ def main():
         if leg.kind == "flop":
             rate = leg.work / (per_call_ms * 1e-3) / 1e12
             d.update({"tflop": round(leg.work / 1e12, 4), "TFLOP/s": round(rate, 1),
-                      "frac_mfma": round(rate / MFMA_BF16_PEAK_TFLOPS, 4)})
+                      "frac_mfma": round(rate / leg.peak, 4)})
+            if leg.peak != MFMA_BF16_PEAK_TFLOPS:
+                d["peak_TFLOP/s"] = leg.peak
         else:
             rate = leg.work / (per_call_ms * 1e-3) / 1e9
             d.update({"GB": round(leg.work / 1e9, 4), "GB/s": round(rate, 1), "frac_hbm": round(rate / HBM_PEAK_GBPS, 4)})
@@ -250,7 +283,7 @@ def main():
     moe_flop = sum(l.work for l in moe_legs)
     moe_ms = sum(l.ms for l in moe_legs) / K
     value = moe_flop / (moe_ms * 1e-3) / 1e12 if moe_ms > 0 else None
-    codec = [l for l in legs if l.kind == "byte" and not l.name.startswith("roundtrip")]
+    codec = [l for l in legs if l.kind == "byte" and not l.name.startswith(("roundtrip", "w4a4."))]
     codec_bytes = sum(l.work * l.reps for l in codec)
     codec_ms = sum(l.ms for l in codec) / K
     hbm_gbps = codec_bytes / (codec_ms * 1e-3) / 1e9 if codec_ms > 0 else None
@@ -258,7 +291,7 @@ def main():
     # dominant kernel: the instantiation with the largest total event time
     by_kernel = {}
     for l in legs:
-        b = by_kernel.setdefault(l.kernel, {"ms": 0.0, "work": 0.0, "launches": 0, "kind": l.kind})
+        b = by_kernel.setdefault(l.kernel, {"ms": 0.0, "work": 0.0, "launches": 0, "kind": l.kind, "peak": l.peak})
         b["ms"] += l.ms / K
         b["work"] += l.work * l.reps
         b["launches"] += l.reps
@@ -266,9 +299,9 @@ def main():
     avg_launch_ms = dom["ms"] / dom["launches"]
     work_per_launch = dom["work"] / dom["launches"]
     if dom["kind"] == "flop":
-        achieved, peak, unit, bound = work_per_launch / (avg_launch_ms * 1e-3) / 1e12, MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+        achieved, peak, unit, bound = work_per_launch / (avg_launch_ms * 1e-3) / 1e12, dom["peak"], "TFLOP/s", "mfma"
     else:
-        achieved, peak, unit, bound = work_per_launch / (avg_launch_ms * 1e-3) / 1e9, HBM_PEAK_GBPS, "GB/s", "hbm"
+        achieved, peak, unit, bound = work_per_launch / (avg_launch_ms * 1e-3) / 1e9, dom["peak"], "GB/s", "hbm"
     traffic = measured_traffic(dom_name)
     roofline = {"bound": bound, "kernel": dom_name, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "avg_launch_us": round(avg_launch_ms * 1e3, 1),
@@ -304,12 +337,31 @@ def main():
                 "legs": "codec legs: kv + bulk"},
         "mfma": {"TFLOP/s": round(value, 1) if value else None,
                  "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4) if value else None},
+        "w4a4": w4a4_summary(legs, K),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "legs": out_legs,
         "setup_s": round(t_gen, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def w4a4_summary(legs, K):
+    """The routed-expert forwards as W4A4: GEMM rate against the fp4 peak, and
+    the rate with the activation quantization counted in."""
+    g = [l for l in legs if l.name.startswith("w4a4.") and l.kind == "flop"]
+    q = [l for l in legs if l.name.startswith("w4a4.") and l.kind == "byte"]
+    if not g:
+        return None
+    flop = sum(l.work for l in g)
+    g_ms, q_ms = sum(l.ms for l in g) / K, sum(l.ms for l in q) / K
+    bf = [l for l in legs if l.name in ("moe.gate_up.fwd", "moe.down.fwd")]
+    bf_ms = sum(l.ms for l in bf) / K
+    return {"gemm_TFLOP/s": round(flop / (g_ms * 1e-3) / 1e12, 1),
+            "frac_fp4": round(flop / (g_ms * 1e-3) / 1e12 / MFMA_FP4_PEAK_TFLOPS, 4),
+            "with_quantize_TFLOP/s": round(flop / ((g_ms + q_ms) * 1e-3) / 1e12, 1),
+            "speedup_vs_bf16_fwd": round(bf_ms / (g_ms + q_ms), 3) if len(bf) == 2 else None,
+            "legs": "w4a4.gate_up + w4a4.down forwards (quantize_mxfp4 of the activations + fp4 MFMA GEMM)"}
 
 
 def measured_traffic(kernel):
