@@ -142,8 +142,9 @@ int mxfp4_grouped_mm_bwd_x(const void* grad_out, int64_t tokens, int64_t n,
 
 /*
  * mxfp4_grouped_mm_fwd_w4a4 -- the forward with the activations in MXFP4 too
- * (W4A4; [MO] reports weight-and-activation FP4 as the variant that reaches
- * the FP4 matrix units, where a dequantize-to-BF16 fallback does not).
+ * (W4A4; [MO] section "The claims, marked reported": weight-and-activation
+ * FP4 is the variant that reaches the FP4 matrix units, where a
+ * dequantize-to-BF16 fallback does not).
  * xq int8 [tokens, k/2] and xs E8M0 [tokens, k/32] are the activations as
  * quantize_mxfp4 writes them ([MX] quantize_mxfp4, the floor rule); weights
  * and offs as in mxfp4_grouped_mm_fwd.  Computes y[rows_e] = dq(xq)[rows_e] @

@@ -668,7 +668,11 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
 
 // ------------------------------------------------------ forward, W4A4
 // y[rows_e] = x_q[rows_e] @ W_e^T with the activations quantized to MXFP4 as
-// well (quantize_mxfp4: packed [T, K/2], E8M0 scales [T, K/32]), on gfx950's
+// well ("NVIDIA Model Optimizer: from mtq.quantize to a 4.95-bit
+// DeepSeek-R1", section "The claims, marked reported": the weight-and-
+// activation FP4 form is the one that runs on the FP4 matrix units; the
+// activations as "nemo_automodel.components.quantization.mxfp4"
+// quantize_mxfp4 writes them: packed [T, K/2], E8M0 scales [T, K/32]), on gfx950's
 // block-scaled MFMA v_mfma_scale_f32_32x32x64_f8f6f4 with both operands fp4
 // e2m1.  Its operand layout (pinned by an in-bounds probe against a float64
 // reference, to fp32 rounding): lane l carries row (or column) l % 32 and

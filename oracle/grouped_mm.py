@@ -92,9 +92,9 @@ def w4a4_activations(x):
     by ``quantize_mxfp4`` (per token row, 32-blocks along K, floor scale rule).
 
     Reading: "NVIDIA Model Optimizer: from mtq.quantize to a 4.95-bit
-    DeepSeek-R1" (the section on weight-only 4-bit against W4A4) names the
-    weight-and-activation FP4 form as the one that runs on the FP4 matrix
-    units, and "nemo_automodel.components.quantization.mxfp4" has one MXFP4
+    DeepSeek-R1", section "The claims, marked reported" (weight-only 4-bit
+    against W4A4), names the weight-and-activation FP4 form as the one that
+    runs on the FP4 matrix units, and "nemo_automodel.components.quantization.mxfp4" has one MXFP4
     quantizer, ``quantize_mxfp4``; the activations of the W4A4 forward are
     taken to be quantized by it.  Each row is independent, so a subset of
     rows can be quantized on its own."""
