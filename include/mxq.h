@@ -104,6 +104,38 @@ int quantize_cache(const void* x, void* out, int t, int64_t rows, int64_t channe
 int quantize_cache_bwd(const void* grad_out, void* grad_in, int t, int64_t numel, void* stream);
 
 /*
+ * quantize_nvfp4 -- [MO] section "NVFP4 in the code: two scales and a
+ * nibble": two-level NVFP4.  x [rows, k] of dtype xt (k % 16 == 0, any
+ * alignment; 16-byte aligned x and 4-byte aligned packed take the fast path)
+ * -> packed uint8 [rows, k/2] (two e2m1 codes per byte, even column in the
+ * low nibble), block_scales uint8 [rows, k/16] (E4M3 bit patterns) and
+ * *global_scale (one float in DEVICE memory, 4-byte aligned).  In fp32,
+ * rounded nearest-even in this order: g = max|x| / 2688 (6 * 448) over the
+ * whole tensor; per block of 16, s_b = E4M3(max|x_b| / fl(6 g)) with a zero
+ * ratio set to 1.0 and then clamped to [2^-9, 448]; d_b = fl(s_b g); codes =
+ * e2m1(fl(x / d_b)) by the midpoints, ties to the even code, saturating at 6,
+ * sign bit for x < 0.  An all-zero tensor gives g = 0, scales 1.0, codes 0.
+ * Inputs must be finite.  *global_scale is also the scratch word of the
+ * tensor max while the call runs (all launches on `stream`).  rows * k == 0
+ * returns MXQ_OK without a launch and leaves *global_scale alone.
+ * Errors: MXQ_ERR_SHAPE (k % 16 != 0 or negative sizes), MXQ_ERR_DTYPE,
+ * MXQ_ERR_NULL, MXQ_ERR_ALIGN (global_scale), MXQ_ERR_ALIAS (any two of the
+ * four buffers overlap), MXQ_ERR_HIP.
+ */
+int quantize_nvfp4(const void* x, int xt, int64_t rows, int64_t k, uint8_t* packed, uint8_t* block_scales,
+                   float* global_scale, void* stream);
+
+/*
+ * dequantize_nvfp4 -- the inverse of quantize_nvfp4 ([MO], same section):
+ * out[i] = fl(e2m1(code_i) * fl(E4M3(s_b) * g)), rounded nearest-even to ot
+ * (code 8 decodes to +0.0; an E4M3 NaN scale gives NaN).  global_scale is a
+ * device pointer to g.  Errors as quantize_nvfp4 (out must not overlap the
+ * inputs).
+ */
+int dequantize_nvfp4(const uint8_t* packed, const uint8_t* block_scales, const float* global_scale, int64_t rows,
+                     int64_t k, void* out, int ot, void* stream);
+
+/*
  * mxfp4_grouped_mm_fwd -- [MX] MXFP4GroupedMM.forward.
  * x bf16 [tokens, k] grouped contiguously by expert; packed [experts, n, k/2]
  * and scales [experts, n, k/32] (mxfp4 weights W_e [n, k], packed along k);

@@ -12,6 +12,7 @@ from .ops import (
     CacheQuantization,
     MXFP4GroupedMM,
     dequantize_mxfp4,
+    dequantize_nvfp4,
     mxfp4_grouped_mm_bwd_x,
     mxfp4_grouped_mm_fwd,
     mxfp4_grouped_mm_fwd_w4a4,
@@ -20,6 +21,7 @@ from .ops import (
     quantize_cache_bwd,
     quantize_cache_forward,
     quantize_mxfp4,
+    quantize_nvfp4,
 )
 
 __all__ = [
@@ -28,4 +30,5 @@ __all__ = [
     "dequantize_mxfp4", "mxfp4_grouped_mm_bwd_x", "mxfp4_grouped_mm_fwd",
     "mxfp4_grouped_mm_fwd_w4a4", "mxfp4_grouped_mm_fwd_w4a4_quantized",
     "quantize_cache", "quantize_cache_bwd", "quantize_cache_forward", "quantize_mxfp4",
+    "quantize_nvfp4", "dequantize_nvfp4",
 ]

@@ -68,6 +68,35 @@ int quantize_cache_bwd(const void* grad_out, void* grad_in, int t, int64_t numel
   return from_hip(mxq::launch_copy(grad_out, grad_in, bytes, (hipStream_t)stream));
 }
 
+int quantize_nvfp4(const void* x, int xt, int64_t rows, int64_t k, uint8_t* packed, uint8_t* block_scales,
+                   float* global_scale, void* stream) {
+  if (rows < 0 || k < 0 || k % 16 != 0) return MXQ_ERR_SHAPE;
+  if (!dtype_ok(xt)) return MXQ_ERR_DTYPE;
+  if (rows == 0 || k == 0) return MXQ_OK;
+  if (!x || !packed || !block_scales || !global_scale) return MXQ_ERR_NULL;
+  if ((uintptr_t)global_scale & 3) return MXQ_ERR_ALIGN;
+  const int64_t n = rows * k, xb = n * dtype_bytes(xt);
+  if (overlap(x, xb, packed, n / 2) || overlap(x, xb, block_scales, n / 16) || overlap(x, xb, global_scale, 4) ||
+      overlap(packed, n / 2, block_scales, n / 16) || overlap(packed, n / 2, global_scale, 4) ||
+      overlap(block_scales, n / 16, global_scale, 4))
+    return MXQ_ERR_ALIAS;
+  return from_hip(mxq::launch_quantize_nvfp4(x, xt, rows, k, packed, block_scales, global_scale, (hipStream_t)stream));
+}
+
+int dequantize_nvfp4(const uint8_t* packed, const uint8_t* block_scales, const float* global_scale, int64_t rows,
+                     int64_t k, void* out, int ot, void* stream) {
+  if (rows < 0 || k < 0 || k % 16 != 0) return MXQ_ERR_SHAPE;
+  if (!dtype_ok(ot)) return MXQ_ERR_DTYPE;
+  if (rows == 0 || k == 0) return MXQ_OK;
+  if (!packed || !block_scales || !global_scale || !out) return MXQ_ERR_NULL;
+  if ((uintptr_t)global_scale & 3) return MXQ_ERR_ALIGN;
+  const int64_t n = rows * k, ob = n * dtype_bytes(ot);
+  if (overlap(out, ob, packed, n / 2) || overlap(out, ob, block_scales, n / 16) || overlap(out, ob, global_scale, 4))
+    return MXQ_ERR_ALIAS;
+  return from_hip(
+      mxq::launch_dequantize_nvfp4(packed, block_scales, global_scale, rows, k, out, ot, (hipStream_t)stream));
+}
+
 static int grouped_mm_check(const void* a, int64_t tokens, int64_t red, const int8_t* packed, const uint8_t* scales,
                             int64_t experts, int64_t other, const int32_t* offs, void* out, int64_t k, int64_t n) {
   if (tokens < 0 || red < 0 || other < 0 || experts < 0) return MXQ_ERR_SHAPE;
@@ -127,7 +156,7 @@ const char* mxq_status_string(int s) {
   switch (s) {
     case MXQ_OK: return "ok";
     case MXQ_ERR_NULL: return "null pointer";
-    case MXQ_ERR_SHAPE: return "bad shape (negative size, k not a multiple of 32, or n not a multiple of 8)";
+    case MXQ_ERR_SHAPE: return "bad shape (negative size, k not a multiple of the block (32 mxfp4, 16 nvfp4, 512 W4A4), n not a multiple of 8, or past a size limit)";
     case MXQ_ERR_DTYPE: return "unsupported dtype";
     case MXQ_ERR_FORMAT: return "unknown format (fp8, mxfp4 or nvfp4)";
     case MXQ_ERR_BLOCK: return "block_size must be positive";

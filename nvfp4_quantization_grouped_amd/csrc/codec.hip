@@ -397,6 +397,245 @@ __global__ void __launch_bounds__(kThreads) k_zero_bytes(uint8_t* __restrict__ d
     dst[i] = 0;
 }
 
+// ---------------------------------------------------------- two-level NVFP4
+// "NVIDIA Model Optimizer: from mtq.quantize to a 4.95-bit DeepSeek-R1",
+// section "NVFP4 in the code: two scales and a nibble":
+//   g   = max|x| / (6 * 448)                       FP32 per-tensor scale
+//   s_b = E4M3(max_{i in b} |x_i| / (6 g))         blocks of 16; a zero scale
+//                                                   becomes 1.0, then clamped to [2^-9, 448]
+//   x^  = E2M1(x / (s_b g)) * s_b g
+// in fp32, each operation rounded nearest-even in the order written.  The
+// divisions are IEEE divisions, not products with a reciprocal: where a
+// quotient falls against the e2m1 midpoints decides the code, so it has to
+// be the correctly rounded one.  Launches: the tensor amax (an atomic max of
+// fp32 bit patterns, which order like the values for x >= 0) into the
+// caller's 4-byte global-scale slot, the block pass reading it, and a
+// one-thread pass that replaces it by g.  A tensor whose amax is 0 has every
+// scale 1.0 and every code 0.
+constexpr float kNvfp4Den = 6.0f * 448.0f;   // 2688, exact
+
+__global__ void k_nvfp4_amax_init(uint32_t* __restrict__ slot) { *slot = 0u; }
+__global__ void k_nvfp4_finalize(uint32_t* __restrict__ slot) { *slot = as_u32(as_f32(*slot) / kNvfp4Den); }
+
+// Wave max, then workgroup max through LDS, then one atomic per workgroup.
+__device__ __forceinline__ void nvfp4_amax_publish(uint32_t m, uint32_t* __restrict__ slot) {
+  m = group_max_u32<64>(m);
+  __shared__ uint32_t wmax[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t b = wmax[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) b = max(b, wmax[i]);
+    if (b) atomicMax(slot, b);
+  }
+}
+
+template <int DT, class M>
+__global__ void __launch_bounds__(kThreads) k_nvfp4_amax(const uint8_t* __restrict__ x, int64_t nchunks,
+                                                       uint32_t* __restrict__ slot) {
+  uint32_t m = 0;
+  const int64_t step = (int64_t)gridDim.x * kThreads * M::kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * M::kUnroll; base < nchunks; base += step) {
+    Chunk<DT> ch[M::kUnroll];
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u) {
+      const int64_t c = base + u * kThreads + threadIdx.x;
+      if (c < nchunks) load_chunk<DT, M>(x, c, ch[u]);
+      else {
+#pragma unroll
+        for (int i = 0; i < Chunk<DT>::kWords; ++i) ch[u].w[i] = 0u;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u) m = max(m, chunk_amax_bits<DT>(ch[u]));
+  }
+  nvfp4_amax_publish(m, slot);
+}
+
+// Block scale of a block with max |x| = ab under the global scale g > 0: its
+// E4M3 bits, and the element divisor d = fl(s_b g).
+__device__ __forceinline__ uint32_t nvfp4_block_scale(float ab, float g, float& d) {
+  float r = ab / (6.0f * g);
+  if (r == 0.0f) r = 1.0f;
+  r = fminf(fmaxf(r, 0x1p-9f), 448.0f);
+  const uint32_t bits = enc_fp8_f2<false>(0u, r, r, 1.0f) & 0xFFu;   // nearest-even E4M3
+  d = dec_fp8_f2<false>(bits, 1.0f).x * g;
+  return bits;
+}
+
+// Eight elements -> eight e2m1 codes of x / d (a code's sign bit is x < 0:
+// -0.0 gives code 0).
+template <int DT>
+__device__ __forceinline__ uint32_t nvfp4_encode_chunk(const Chunk<DT>& ch, float d) {
+  float v[8];
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = as_f32(ch.w[i]);
+  } else if constexpr (DT == DT_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_lo(ch.w[i]); v[2 * i + 1] = bf16_hi(ch.w[i]); }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[2 * i] = f16_lo(ch.w[i]); v[2 * i + 1] = f16_hi(ch.w[i]); }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = v[i] / d + 0.0f;
+  uint32_t c = 0;
+  c = enc_fp4_f2<0>(c, v[0], v[1], 1.0f);
+  c = enc_fp4_f2<1>(c, v[2], v[3], 1.0f);
+  c = enc_fp4_f2<2>(c, v[4], v[5], 1.0f);
+  c = enc_fp4_f2<3>(c, v[6], v[7], 1.0f);
+  return c;
+}
+
+template <int DT, class M>
+__global__ void __launch_bounds__(kThreads) k_quantize_nvfp4(const uint8_t* __restrict__ x, uint32_t* __restrict__ packed,
+                                                           uint8_t* __restrict__ scales, int64_t nchunks,
+                                                           const uint32_t* __restrict__ slot) {
+  const float g = as_f32(*slot) / kNvfp4Den;
+  const int64_t step = (int64_t)gridDim.x * kThreads * M::kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * M::kUnroll; base < nchunks; base += step) {
+    Chunk<DT> ch[M::kUnroll];
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u) {
+      const int64_t c = base + u * kThreads + threadIdx.x;
+      if (c < nchunks) load_chunk<DT, M>(x, c, ch[u]);
+      else {
+#pragma unroll
+        for (int i = 0; i < Chunk<DT>::kWords; ++i) ch[u].w[i] = 0u;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u) {
+      const int64_t c = base + u * kThreads + threadIdx.x;
+      const uint32_t ab = group_max_u32<2>(chunk_amax_bits<DT>(ch[u]));   // 16 = 2 chunks
+      uint32_t codes = 0u, sbits = 0x38u;                                  // g = 0: scale 1.0, codes 0
+      if (g != 0.0f) {
+        float d;
+        sbits = nvfp4_block_scale(as_f32(ab), g, d);
+        codes = nvfp4_encode_chunk<DT>(ch[u], d);
+      }
+      if (c < nchunks) {
+        M::st(codes, packed + c);
+        if ((c & 1) == 0) scales[c >> 1] = (uint8_t)sbits;
+      }
+    }
+  }
+}
+
+// fp32 product a * b, kept as an fp32 value: without the empty asm the
+// compiler folds a product that is then narrowed to f16 into one
+// mixed-precision multiply-add (with a +0.0 addend, which turns -0.0 into
+// +0.0, and one rounding where the method rounds to fp32 first).
+__device__ __forceinline__ float mul_f32(float a, float b) {
+  float r = a * b;
+  asm volatile("" : "+v"(r));
+  return r;
+}
+
+// fp32 pair -> bf16 pair, nearest-even.
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Eight codes (code 8 already cleared) times d -> eight values of DT.
+template <int DT>
+__device__ __forceinline__ void nvfp4_decode_chunk(uint32_t c, float d, Chunk<DT>& out) {
+  float v[8];
+  const uint32_t b[4] = {dec_fp4_bf16x2<0>(c, 1.0f), dec_fp4_bf16x2<1>(c, 1.0f), dec_fp4_bf16x2<2>(c, 1.0f),
+                         dec_fp4_bf16x2<3>(c, 1.0f)};   // e2m1 values, exact in bf16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[2 * i] = mul_f32(bf16_lo(b[i]), d); v[2 * i + 1] = mul_f32(bf16_hi(b[i]), d); }
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out.w[i] = as_u32(v[i]);
+  } else if constexpr (DT == DT_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out.w[i] = pack_bf16x2_rne(v[2 * i], v[2 * i + 1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out.w[i] = pack_f16x2(v[2 * i], v[2 * i + 1]);
+  }
+}
+
+template <int DT, class M>
+__global__ void __launch_bounds__(kThreads) k_dequantize_nvfp4(const uint32_t* __restrict__ packed,
+                                                             const uint8_t* __restrict__ scales,
+                                                             const float* __restrict__ gscale,
+                                                             uint8_t* __restrict__ out, int64_t nchunks) {
+  const float g = *gscale;
+  const int64_t step = (int64_t)gridDim.x * kThreads * M::kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * M::kUnroll; base < nchunks; base += step) {
+    uint32_t codes[M::kUnroll], sb[M::kUnroll];
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u) {
+      const int64_t c = base + u * kThreads + threadIdx.x;
+      codes[u] = c < nchunks ? M::ld(packed + c) : 0u;
+      sb[u] = c < nchunks ? (uint32_t)scales[c >> 1] : 0x38u;
+    }
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u) {
+      const int64_t c = base + u * kThreads + threadIdx.x;
+      Chunk<DT> o;
+      nvfp4_decode_chunk<DT>(clear_negzero_codes(codes[u]), dec_fp8_f2<false>(sb[u], 1.0f).x * g, o);
+      if (c < nchunks) store_chunk<DT, M>(out, c, o);
+    }
+  }
+}
+
+// General paths (any alignment): one element / one 16-element block per thread.
+template <int DT>
+__global__ void __launch_bounds__(kThreads) k_nvfp4_amax_general(const uint8_t* __restrict__ x, int64_t n,
+                                                               uint32_t* __restrict__ slot) {
+  uint32_t m = 0;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads)
+    m = max(m, as_u32(load_elem<DT>(x, i)) & 0x7FFFFFFFu);
+  nvfp4_amax_publish(m, slot);
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kThreads) k_quantize_nvfp4_general(const uint8_t* __restrict__ x,
+                                                                   uint8_t* __restrict__ packed,
+                                                                   uint8_t* __restrict__ scales, int64_t nblocks,
+                                                                   const uint32_t* __restrict__ slot) {
+  const float g = as_f32(*slot) / kNvfp4Den;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += (int64_t)gridDim.x * kThreads) {
+    uint32_t ab = 0;
+    for (int i = 0; i < 16; ++i) ab = max(ab, as_u32(load_elem<DT>(x, b * 16 + i)) & 0x7FFFFFFFu);
+    if (g == 0.0f) {
+      for (int j = 0; j < 8; ++j) packed[b * 8 + j] = 0;
+      scales[b] = 0x38;
+      continue;
+    }
+    float d;
+    scales[b] = (uint8_t)nvfp4_block_scale(as_f32(ab), g, d);
+    for (int j = 0; j < 8; ++j) {
+      const float q0 = load_elem<DT>(x, b * 16 + 2 * j) / d + 0.0f, q1 = load_elem<DT>(x, b * 16 + 2 * j + 1) / d + 0.0f;
+      packed[b * 8 + j] = (uint8_t)(enc_fp4_f2<0>(0u, q0, q1, 1.0f) & 0xFFu);
+    }
+  }
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kThreads) k_dequantize_nvfp4_general(const uint8_t* __restrict__ packed,
+                                                                     const uint8_t* __restrict__ scales,
+                                                                     const float* __restrict__ gscale,
+                                                                     uint8_t* __restrict__ out, int64_t nblocks) {
+  const float g = *gscale;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += (int64_t)gridDim.x * kThreads) {
+    const float d = dec_fp8_f2<false>((uint32_t)scales[b], 1.0f).x * g;
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t h = dec_fp4_bf16x2<0>(clear_negzero_codes((uint32_t)packed[b * 8 + j]), 1.0f);
+      const float v0 = mul_f32(bf16_lo(h), d), v1 = mul_f32(bf16_hi(h), d);
+      const uint32_t bb = pack_bf16x2_rne(v0, v1);
+      store_elem<DT>(out, b * 16 + 2 * j, v0, bb & 0xFFFFu);
+      store_elem<DT>(out, b * 16 + 2 * j + 1, v1, bb >> 16);
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 static inline int grid_for(int64_t items, int64_t per_block) {
   const int64_t cap = kGridCap;
@@ -537,6 +776,69 @@ hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st
 hipError_t launch_zero(void* dst, int64_t bytes, hipStream_t st) {
   hipLaunchKernelGGL(k_zero_bytes, dim3(grid_for(bytes, kThreads * 4)), dim3(kThreads), 0, st, (uint8_t*)dst, bytes);
   return hipGetLastError();
+}
+
+template <int DT, class M>
+static void launch_nvfp4_fast(const void* x, int64_t nchunks, uint32_t* packed, uint8_t* scales, uint32_t* slot,
+                              hipStream_t st) {
+  const int g = grid_for(nchunks, kThreads * M::kUnroll);
+  hipLaunchKernelGGL((k_nvfp4_amax<DT, M>), dim3(g), dim3(kThreads), 0, st, (const uint8_t*)x, nchunks, slot);
+  hipLaunchKernelGGL((k_quantize_nvfp4<DT, M>), dim3(g), dim3(kThreads), 0, st, (const uint8_t*)x, packed, scales,
+                     nchunks, (const uint32_t*)slot);
+}
+
+template <int DT>
+static hipError_t launch_quantize_nvfp4_t(const void* x, int64_t rows, int64_t k, uint8_t* packed, uint8_t* scales,
+                                          float* gscale, hipStream_t st) {
+  const int64_t n = rows * k;
+  uint32_t* slot = reinterpret_cast<uint32_t*>(gscale);
+  hipLaunchKernelGGL(k_nvfp4_amax_init, dim3(1), dim3(1), 0, st, slot);
+  if (aligned(x, 16) && aligned(packed, 4)) {
+    const int64_t nchunks = n / 8, bytes = n * (DT == DT_F32 ? 4 : 2);
+    if (bytes >= kBigStreamBytes) launch_nvfp4_fast<DT, StreamBig>(x, nchunks, (uint32_t*)packed, scales, slot, st);
+    else if (bytes >= kTinyStreamBytes) launch_nvfp4_fast<DT, StreamSmall>(x, nchunks, (uint32_t*)packed, scales, slot, st);
+    else launch_nvfp4_fast<DT, StreamTiny>(x, nchunks, (uint32_t*)packed, scales, slot, st);
+  } else {
+    hipLaunchKernelGGL(k_nvfp4_amax_general<DT>, dim3(grid_for(n, kThreads * 16)), dim3(kThreads), 0, st,
+                       (const uint8_t*)x, n, slot);
+    hipLaunchKernelGGL(k_quantize_nvfp4_general<DT>, dim3(grid_for(n / 16, kThreads)), dim3(kThreads), 0, st,
+                       (const uint8_t*)x, packed, scales, n / 16, (const uint32_t*)slot);
+  }
+  hipLaunchKernelGGL(k_nvfp4_finalize, dim3(1), dim3(1), 0, st, slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_nvfp4(const void* x, int dt, int64_t rows, int64_t k, uint8_t* packed, uint8_t* scales,
+                                 float* global_scale, hipStream_t st) {
+  switch (dt) {
+    case DT_F32: return launch_quantize_nvfp4_t<DT_F32>(x, rows, k, packed, scales, global_scale, st);
+    case DT_BF16: return launch_quantize_nvfp4_t<DT_BF16>(x, rows, k, packed, scales, global_scale, st);
+    default: return launch_quantize_nvfp4_t<DT_F16>(x, rows, k, packed, scales, global_scale, st);
+  }
+}
+
+template <int DT>
+static hipError_t launch_dequantize_nvfp4_t(const uint8_t* packed, const uint8_t* scales, const float* gscale,
+                                            int64_t rows, int64_t k, void* out, hipStream_t st) {
+  const int64_t n = rows * k;
+  if (aligned(packed, 4) && aligned(out, 16)) {
+    const int64_t nchunks = n / 8;
+    hipLaunchKernelGGL((k_dequantize_nvfp4<DT, StreamDequant>), dim3(grid_for(nchunks, kThreads * StreamDequant::kUnroll)),
+                       dim3(kThreads), 0, st, (const uint32_t*)packed, scales, gscale, (uint8_t*)out, nchunks);
+  } else {
+    hipLaunchKernelGGL(k_dequantize_nvfp4_general<DT>, dim3(grid_for(n / 16, kThreads)), dim3(kThreads), 0, st,
+                       packed, scales, gscale, (uint8_t*)out, n / 16);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_nvfp4(const uint8_t* packed, const uint8_t* scales, const float* global_scale,
+                                   int64_t rows, int64_t k, void* out, int dt, hipStream_t st) {
+  switch (dt) {
+    case DT_F32: return launch_dequantize_nvfp4_t<DT_F32>(packed, scales, global_scale, rows, k, out, st);
+    case DT_BF16: return launch_dequantize_nvfp4_t<DT_BF16>(packed, scales, global_scale, rows, k, out, st);
+    default: return launch_dequantize_nvfp4_t<DT_F16>(packed, scales, global_scale, rows, k, out, st);
+  }
 }
 
 }  // namespace mxq

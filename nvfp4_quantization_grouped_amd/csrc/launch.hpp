@@ -14,6 +14,11 @@ hipError_t launch_dequantize_mxfp4(const int8_t* packed, const uint8_t* scales, 
                                    int dt, hipStream_t st);
 hipError_t launch_quantize_cache(const void* x, void* out, int dt, int64_t rows, int64_t channels, int fmt,
                                  int32_t block, hipStream_t st);
+// Two-level NVFP4: packed e2m1 [n/2], E4M3 block-16 scales [n/16], FP32 global scale (1 float, device).
+hipError_t launch_quantize_nvfp4(const void* x, int dt, int64_t rows, int64_t k, uint8_t* packed, uint8_t* scales,
+                                 float* global_scale, hipStream_t st);
+hipError_t launch_dequantize_nvfp4(const uint8_t* packed, const uint8_t* scales, const float* global_scale,
+                                   int64_t rows, int64_t k, void* out, int dt, hipStream_t st);
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
 hipError_t launch_zero(void* dst, int64_t bytes, hipStream_t st);
 // bwd = false: out[T, N] = a[T, K] W_e^T;  bwd = true: out[T, K] = a[T, N] W_e.

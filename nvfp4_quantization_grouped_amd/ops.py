@@ -10,6 +10,9 @@ Names and signatures follow the pages:
   ``dequantize_mxfp4``, ``MXFP4GroupedMM``, ``MXFP4_BLOCK_SIZE``.
 * "nemo_automodel.components.models.deepseek_v41.quantization":
   ``quantize_cache`` and ``_CacheQuantization``.
+* "NVIDIA Model Optimizer: from mtq.quantize to a 4.95-bit DeepSeek-R1":
+  ``quantize_nvfp4`` / ``dequantize_nvfp4`` (two-level NVFP4) and the W4A4
+  forward ``mxfp4_grouped_mm_fwd_w4a4``.
 """
 
 import torch
@@ -85,6 +88,58 @@ def dequantize_mxfp4(packed, scales, dtype):
     with torch.cuda.device(p.device):
         st = _lib.lib().dequantize_mxfp4(_ptr(p), _ptr(s), rows, K, _ptr(out), _DT[dtype], _stream(p.device))
     _lib.check(st, "dequantize_mxfp4")
+    return out
+
+
+_E4M3 = getattr(torch, "float8_e4m3fn", None)
+
+
+def quantize_nvfp4(x):
+    """Two-level NVFP4 ("NVIDIA Model Optimizer: from mtq.quantize to a
+    4.95-bit DeepSeek-R1", section "NVFP4 in the code: two scales and a
+    nibble"): [..., K] float tensor (K % 16 == 0) -> (uint8 packed [..., K/2],
+    float8_e4m3fn block scales [..., K/16], float32 global scale g [] on the
+    device), the four-tensor checkpoint layout's weight, weight_scale and
+    weight_scale_2."""
+    _need_cuda(x)
+    if x.dtype not in _DT:
+        raise TypeError(f"quantize_nvfp4: unsupported dtype {x.dtype}")
+    K = x.shape[-1] if x.dim() else 0
+    if K % 16:
+        raise ValueError("quantize_nvfp4: K must be divisible by 16")
+    x = x.contiguous()
+    rows = x.numel() // K if K else 0
+    packed = torch.empty(*x.shape[:-1], K // 2, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(*x.shape[:-1], K // 16, dtype=torch.uint8, device=x.device)
+    g = torch.zeros((), dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        st = _lib.lib().quantize_nvfp4(_ptr(x), _DT[x.dtype], rows, K, _ptr(packed), _ptr(scales), g.data_ptr(),
+                                       _stream(x.device))
+    _lib.check(st, "quantize_nvfp4")
+    return packed, (scales.view(_E4M3) if _E4M3 is not None else scales), g
+
+
+def dequantize_nvfp4(packed, block_scales, global_scale, dtype):
+    """uint8 packed [..., K/2] + E4M3 block scales [..., K/16] + float32 global
+    scale (a device scalar) -> [..., K] in ``dtype``."""
+    _need_cuda(packed, block_scales, global_scale)
+    if dtype not in _DT:
+        raise TypeError(f"dequantize_nvfp4: unsupported dtype {dtype}")
+    s = block_scales.view(torch.uint8) if block_scales.dtype != torch.uint8 else block_scales
+    s = s.contiguous()
+    p = packed.contiguous()
+    g = global_scale.to(torch.float32).contiguous()
+    if g.numel() != 1:
+        raise ValueError("dequantize_nvfp4: global_scale must hold one value")
+    K = p.shape[-1] * 2
+    if tuple(s.shape) != tuple(p.shape[:-1]) + (K // 16,):
+        raise ValueError("dequantize_nvfp4: block scales must be [..., K/16] for packed [..., K/2]")
+    rows = p.numel() * 2 // K if K else 0
+    out = torch.empty(*p.shape[:-1], K, dtype=dtype, device=p.device)
+    with torch.cuda.device(p.device):
+        st = _lib.lib().dequantize_nvfp4(_ptr(p), _ptr(s), g.data_ptr(), rows, K, _ptr(out), _DT[dtype],
+                                         _stream(p.device))
+    _lib.check(st, "dequantize_nvfp4")
     return out
 
 

@@ -99,6 +99,27 @@ def test_grouped_mm_validation(L):
     assert b(FAKE, 1, 1 << 16, FAKE * 2, FAKE * 3, 2, 1 << 16, FAKE * 4, FAKE * 5, None) == -2
 
 
+def test_nvfp4_validation(L):
+    q = L.quantize_nvfp4
+    # (x, dtype, rows, k, packed, block_scales, global_scale, stream)
+    assert q(FAKE, 1, 4, 24, FAKE * 2, FAKE * 3, FAKE * 4, None) == -2     # k % 16
+    assert q(FAKE, 1, -1, 32, FAKE * 2, FAKE * 3, FAKE * 4, None) == -2
+    assert q(FAKE, 7, 4, 32, FAKE * 2, FAKE * 3, FAKE * 4, None) == -3     # dtype
+    assert q(FAKE, 1, 4, 32, FAKE * 2, FAKE * 3, None, None) == -1
+    assert q(FAKE, 1, 4, 32, FAKE * 2, FAKE * 3, FAKE * 4 + 2, None) == -6   # global scale 4-byte aligned
+    assert q(FAKE, 1, 4, 32, FAKE + 8, FAKE * 3, FAKE * 4, None) == -7       # packed inside x
+    assert q(FAKE, 1, 4, 32, FAKE * 2, FAKE * 3, FAKE * 2 + 4, None) == -7   # global scale inside packed
+    assert q(FAKE, 1, 0, 32, FAKE * 2, FAKE * 3, FAKE * 4, None) == 0        # nothing to do
+    d = L.dequantize_nvfp4
+    # (packed, block_scales, global_scale, rows, k, out, dtype, stream)
+    assert d(FAKE, FAKE * 2, FAKE * 3, 4, 40, FAKE * 4, 1, None) == -2
+    assert d(FAKE, FAKE * 2, FAKE * 3, 4, 32, FAKE * 4, 9, None) == -3
+    assert d(FAKE, None, FAKE * 3, 4, 32, FAKE * 4, 1, None) == -1
+    assert d(FAKE, FAKE * 2, FAKE * 3 + 1, 4, 32, FAKE * 4, 1, None) == -6
+    assert d(FAKE, FAKE * 2, FAKE * 3, 4, 32, FAKE - 16, 1, None) == -7      # out over packed
+    assert d(FAKE, FAKE * 2, FAKE * 3, 0, 32, FAKE * 4, 1, None) == 0
+
+
 def test_grouped_mm_w4a4_validation(L):
     f = L.mxfp4_grouped_mm_fwd_w4a4
     # (xq, xs, tokens, k, packed, scales, experts, n, offs, y, stream)
