@@ -10,6 +10,8 @@
 // non-temporally; 4 otherwise).  The general path (misaligned pointers, block sizes that
 // are not a power of two in [8, 512], partial final groups) is one thread per
 // block with scalar accesses; it shares the element arithmetic.
+#include <algorithm>
+
 #include "launch.hpp"
 #include "mxq_device.hpp"
 
@@ -464,8 +466,19 @@ __device__ __forceinline__ uint32_t nvfp4_block_scale(float ab, float g, float& 
   return bits;
 }
 
-// Eight elements -> eight e2m1 codes of x / d (a code's sign bit is x < 0:
-// -0.0 gives code 0).
+// Eight elements -> eight e2m1 codes of the correctly rounded x / d (a
+// code's sign bit is x < 0: -0.0 gives code 0).  Fast form: with r the
+// hardware reciprocal of d (within 1 ulp), x r is within ~2.5 ulp of x / d, so the codes of
+// x r nudged down and up by 2^-20 (8 ulp) bracket the code of fl(x / d);
+// where the two agree no e2m1 midpoint lies between them and that is the
+// code.  A code of magnitude 0 keeps the sign of fl(x / d), which is -0.0
+// (code 0) for a negative x with |x / d| <= 2^-150, a boundary the
+// reciprocal product cannot see; with d < 256 only nonzero fp32 subnormal
+// inputs are that small (bf16 and f16 values are not).  So chunks with an
+// element within reach of a midpoint (exact ties among them), with d >= 256
+// or a reciprocal past 2^126, or with a nonzero fp32 subnormal input take
+// IEEE divisions.  About half the VALU work of a division per element, and
+// this pass is bound by it.
 template <int DT>
 __device__ __forceinline__ uint32_t nvfp4_encode_chunk(const Chunk<DT>& ch, float d) {
   float v[8];
@@ -480,12 +493,33 @@ __device__ __forceinline__ uint32_t nvfp4_encode_chunk(const Chunk<DT>& ch, floa
     for (int i = 0; i < 4; ++i) { v[2 * i] = f16_lo(ch.w[i]); v[2 * i + 1] = f16_hi(ch.w[i]); }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = v[i] / d + 0.0f;
+  for (int i = 0; i < 8; ++i) v[i] += 0.0f;   // -0.0 -> +0.0
+  const float r = __builtin_amdgcn_rcpf(d);
+  constexpr float kDown = 1.0f - 0x1p-20f, kUp = 1.0f + 0x1p-20f;
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = v[i] * r;
+  uint32_t lo = 0, hi = 0;
+  lo = enc_fp4_f2<0>(lo, q[0] * kDown, q[1] * kDown, 1.0f);
+  hi = enc_fp4_f2<0>(hi, q[0] * kUp, q[1] * kUp, 1.0f);
+  lo = enc_fp4_f2<1>(lo, q[2] * kDown, q[3] * kDown, 1.0f);
+  hi = enc_fp4_f2<1>(hi, q[2] * kUp, q[3] * kUp, 1.0f);
+  lo = enc_fp4_f2<2>(lo, q[4] * kDown, q[5] * kDown, 1.0f);
+  hi = enc_fp4_f2<2>(hi, q[4] * kUp, q[5] * kUp, 1.0f);
+  lo = enc_fp4_f2<3>(lo, q[6] * kDown, q[7] * kDown, 1.0f);
+  hi = enc_fp4_f2<3>(hi, q[6] * kUp, q[7] * kUp, 1.0f);
+  bool exact = !(r <= 0x1p126f) || !(d < 256.0f);
+  if constexpr (DT == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) exact |= ((as_u32(v[i]) & 0x7FFFFFFFu) - 1u) < 0x007FFFFFu;   // nonzero subnormal
+  }
+  if (lo == hi && !exact) return lo;
+  // (+ 0.0f: a quotient that underflows to -0.0 gets code 0)
   uint32_t c = 0;
-  c = enc_fp4_f2<0>(c, v[0], v[1], 1.0f);
-  c = enc_fp4_f2<1>(c, v[2], v[3], 1.0f);
-  c = enc_fp4_f2<2>(c, v[4], v[5], 1.0f);
-  c = enc_fp4_f2<3>(c, v[6], v[7], 1.0f);
+  c = enc_fp4_f2<0>(c, v[0] / d + 0.0f, v[1] / d + 0.0f, 1.0f);
+  c = enc_fp4_f2<1>(c, v[2] / d + 0.0f, v[3] / d + 0.0f, 1.0f);
+  c = enc_fp4_f2<2>(c, v[4] / d + 0.0f, v[5] / d + 0.0f, 1.0f);
+  c = enc_fp4_f2<3>(c, v[6] / d + 0.0f, v[7] / d + 0.0f, 1.0f);
   return c;
 }
 
@@ -778,11 +812,16 @@ hipError_t launch_zero(void* dst, int64_t bytes, hipStream_t st) {
   return hipGetLastError();
 }
 
+// At most 1024 workgroups for the amax pass: each ends with one atomic on
+// the same word, and 16384 of them (the streaming cap) measured 35% slower.
+constexpr int kAmaxGridCap = 1024;
+
 template <int DT, class M>
 static void launch_nvfp4_fast(const void* x, int64_t nchunks, uint32_t* packed, uint8_t* scales, uint32_t* slot,
                               hipStream_t st) {
   const int g = grid_for(nchunks, kThreads * M::kUnroll);
-  hipLaunchKernelGGL((k_nvfp4_amax<DT, M>), dim3(g), dim3(kThreads), 0, st, (const uint8_t*)x, nchunks, slot);
+  hipLaunchKernelGGL((k_nvfp4_amax<DT, M>), dim3(std::min(g, kAmaxGridCap)), dim3(kThreads), 0, st, (const uint8_t*)x,
+                     nchunks, slot);
   hipLaunchKernelGGL((k_quantize_nvfp4<DT, M>), dim3(g), dim3(kThreads), 0, st, (const uint8_t*)x, packed, scales,
                      nchunks, (const uint32_t*)slot);
 }
@@ -799,7 +838,7 @@ static hipError_t launch_quantize_nvfp4_t(const void* x, int64_t rows, int64_t k
     else if (bytes >= kTinyStreamBytes) launch_nvfp4_fast<DT, StreamSmall>(x, nchunks, (uint32_t*)packed, scales, slot, st);
     else launch_nvfp4_fast<DT, StreamTiny>(x, nchunks, (uint32_t*)packed, scales, slot, st);
   } else {
-    hipLaunchKernelGGL(k_nvfp4_amax_general<DT>, dim3(grid_for(n, kThreads * 16)), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL(k_nvfp4_amax_general<DT>, dim3(std::min(grid_for(n, kThreads * 16), kAmaxGridCap)), dim3(kThreads), 0, st,
                        (const uint8_t*)x, n, slot);
     hipLaunchKernelGGL(k_quantize_nvfp4_general<DT>, dim3(grid_for(n / 16, kThreads)), dim3(kThreads), 0, st,
                        (const uint8_t*)x, packed, scales, n / 16, (const uint32_t*)slot);
