@@ -217,6 +217,17 @@ def main():
             legs.append(Leg(f"bulk.quantize_cache.{fmt}", f"k_quantize_cache<bf16,{fmt},{block // 8}>", "byte", 4.0 * nb,
                             lambda i, code=code, block=block: check(
                                 L.quantize_cache(bx.data_ptr(), bco.data_ptr(), 1, br, bc, code, block, sp), "qc")))
+        # two-level NVFP4: the tensor max must be known before any block is
+        # scaled, so the input is read twice (algorithmic bytes: 2 reads + outputs)
+        npk = torch.empty(br, bc // 2, dtype=torch.uint8, device=dev)
+        nsc = torch.empty(br, bc // 16, dtype=torch.uint8, device=dev)
+        ng = torch.zeros(1, dtype=torch.float32, device=dev)
+        legs.append(Leg("bulk.quantize_nvfp4", "k_nvfp4_amax+k_quantize_nvfp4<bf16>", "byte", nb * (2 * 2 + 0.5 + 1 / 16),
+                        lambda i: check(L.quantize_nvfp4(bx.data_ptr(), 1, br, bc, npk.data_ptr(), nsc.data_ptr(),
+                                                         ng.data_ptr(), sp), "qnv")))
+        legs.append(Leg("bulk.dequantize_nvfp4", "k_dequantize_nvfp4<bf16>", "byte", nb * (0.5 + 1 / 16 + 2),
+                        lambda i: check(L.dequantize_nvfp4(npk.data_ptr(), nsc.data_ptr(), ng.data_ptr(), br, bc,
+                                                           bdq.data_ptr(), 1, sp), "dqnv")))
         nw = 64 * 4096 * 4096
         legs.append(Leg("bulk.weight_dequant", "k_dequantize_mxfp4<bf16>", "byte", nw * (0.5 + 1 / 32 + 2),
                         lambda i: check(L.dequantize_mxfp4(wp.data_ptr(), ws.data_ptr(), 64 * 4096, 4096,
@@ -328,7 +339,8 @@ def main():
         "config": {
             "workload": "routed-expert layer share (32 experts, hidden 7168, intermediate 2048, 131072 routed rows, "
                         "fwd + grad_x) + 8-expert GEMM [4096x4096 -> 2048] + bf16 KV cache [4,8192,512] fake-quant "
-                        "fp8/128, mxfp4/32, nvfp4/16 + STE + bulk bf16 [65536,7168] codecs + [64,4096,4096] weight dequant",
+                        "fp8/128, mxfp4/32, nvfp4/16 + STE + bulk bf16 [65536,7168] codecs (mxfp4, two-level nvfp4, "
+                        "cache fake-quant) + [64,4096,4096] weight dequant + W4A4 routed-expert forwards",
             "value_is": "grouped-GEMM TFLOP/s of the routed-expert layer legs (event time)",
             "moe_rows": moe_rows,
         },
