@@ -43,7 +43,8 @@ from .formats import (
     from_dtype_bits,
 )
 from .mxfp4 import quantize_mxfp4, dequantize_mxfp4, floor_scale_exponent
-from .cache import power_of_two_ceiling, cache_scale, quantize_cache, quantize_cache_backward
+from .cache import (power_of_two_ceiling, cache_scale, quantize_cache, quantize_cache_backward, quantize_cache_packed,
+                    dequantize_cache_packed)
 from .nvfp4 import (global_scale as nvfp4_global_scale, e4m3_bits, e4m3_decode, encode_with_global_scale as nvfp4_encode,
                     quantize_nvfp4, dequantize_nvfp4_values, dequantize_nvfp4)
 from .grouped_mm import (dequantize_expert_weights, grouped_mm_fwd, grouped_mm_bwd_x, grouped_mm_rows, segments,
@@ -55,6 +56,7 @@ __all__ = [
     "to_dtype_bits", "from_dtype_bits",
     "quantize_mxfp4", "dequantize_mxfp4", "floor_scale_exponent",
     "power_of_two_ceiling", "cache_scale", "quantize_cache", "quantize_cache_backward",
+    "quantize_cache_packed", "dequantize_cache_packed",
     "dequantize_expert_weights", "grouped_mm_fwd", "grouped_mm_bwd_x", "grouped_mm_rows", "segments",
     "w4a4_activations", "grouped_mm_fwd_w4a4",
     "nvfp4_global_scale", "e4m3_bits", "e4m3_decode", "nvfp4_encode", "quantize_nvfp4", "dequantize_nvfp4_values",

@@ -24,6 +24,11 @@ Readings taken where the page is open:
   scale) is rounded nearest-even to the input dtype.
 * Any block size is accepted for every format; the page uses 32 for SWA and the
   indexer and 16 for compressed KV.
+* Packed storage (``quantize_cache_packed``): the page keeps only the
+  round-tripped values.  Storing the codes and the per-group scale bytes that
+  round trip passes through (e2m1 nibbles or E4M3 bytes; E8M0 or E4M3 scale
+  bytes) is the plainest packed form; it needs whole groups, and decoding it
+  gives the fake-quantized tensor bit for bit.
 """
 
 import numpy as np
@@ -94,6 +99,66 @@ def quantize_cache(x, fmt, block_size, dtype):
     of ``dtype`` ('f32' | 'bf16' | 'f16'); returns raw bit patterns of a new
     tensor of the same shape and dtype.  The input array is not modified."""
     return to_dtype_bits(quantize_cache_values(x, fmt, block_size), dtype)
+
+
+def quantize_cache_packed(x, fmt, block_size):
+    """The encoding ``quantize_cache`` rounds through, stored instead of
+    multiplied back (packed KV-cache storage): x float64 [..., C] with whole
+    groups only (C % block_size == 0; even block_size for the fp4 formats).
+
+    Returns (codes, scales):
+    * mxfp4 / nvfp4: codes uint8 [..., C/2], e2m1, two per byte with the even
+      channel in the low nibble, sign bit for x < 0 (as ``quantize_mxfp4``);
+      fp8: codes uint8 [..., C], E4M3 (FN) bit patterns, sign kept;
+    * scales uint8 [..., C/block_size]: the group's power-of-two scale 2^k as
+      an E8M0 byte k + 127 (mxfp4, fp8) or as E4M3 bits (nvfp4, whose scales
+      are clamped into E4M3's powers of two 2^-9..2^8).
+    Reading: the page keeps only the round-tripped values; storing the codes
+    and scales the round trip goes through is the packed form, and
+    ``dequantize_cache_packed`` of it equals ``quantize_cache`` bit for bit."""
+    from .nvfp4 import e4m3_bits
+    if fmt not in FORMAT_FMAX:
+        raise ValueError("quantize_cache_packed: format must be fp8, mxfp4 or nvfp4")
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("quantize_cache_packed: non-finite input")
+    C = x.shape[-1]
+    if block_size <= 0 or C % block_size or (fmt != "fp8" and block_size % 2):
+        raise ValueError("quantize_cache_packed: whole groups of a positive (even for fp4) block size")
+    lead = x.shape[:-1]
+    blocks = x.reshape(lead + (C // block_size, block_size))
+    amax = np.max(np.abs(blocks), axis=-1)
+    s = cache_scale(amax, fmt)
+    q = blocks / s[..., None]                      # exact: s is a power of two
+    if fmt == "fp8":
+        v = e4m3_round(q).reshape(lead + (C,))
+        codes = (e4m3_bits(np.abs(v)) | (np.signbit(v).astype(np.uint8) << 7)).astype(np.uint8)
+    else:
+        c = e2m1_encode(q).reshape(lead + (C,))
+        codes = (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+    if fmt == "nvfp4":
+        scales = e4m3_bits(s)
+    else:
+        _, ex = np.frexp(s)                        # s = 2^(ex-1)
+        scales = (ex.astype(np.int64) - 1 + 127).astype(np.uint8)
+    return codes, scales
+
+
+def dequantize_cache_packed(codes, scales, fmt, block_size, dtype):
+    """Values of the packed form: code value (e2m1 table, code 8 -> +0.0; or
+    E4M3) times the group's scale, rounded to ``dtype``; raw bit patterns."""
+    from .nvfp4 import e4m3_decode
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    if fmt == "fp8":
+        vals = e4m3_decode(codes)
+    else:
+        vals = np.stack([E2M1_TABLE[codes & 15], E2M1_TABLE[codes >> 4]], axis=-1).reshape(
+            codes.shape[:-1] + (codes.shape[-1] * 2,))
+    s = e4m3_decode(scales) if fmt == "nvfp4" else np.ldexp(1.0, scales.astype(np.int64) - 127)
+    C = vals.shape[-1]
+    out = vals.reshape(vals.shape[:-1] + (C // block_size, block_size)) * s[..., None]
+    return to_dtype_bits(out.reshape(vals.shape), dtype)
 
 
 def quantize_cache_backward(grad):

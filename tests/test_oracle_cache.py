@@ -164,3 +164,90 @@ def test_bad_arguments():
         quantize_cache_values(np.zeros((2, 32)), "int4", 32)
     with pytest.raises(ValueError):
         quantize_cache_values(np.zeros((2, 32)), "fp8", 0)
+
+
+# ---- packed KV-cache storage: the codes and scales the fake-quant goes through
+
+PACKED_CASES = [("fp8", 8), ("fp8", 24), ("fp8", 128), ("mxfp4", 8), ("mxfp4", 32), ("mxfp4", 512),
+                ("nvfp4", 16), ("nvfp4", 64), ("nvfp4", 6)]
+
+
+def _wide(seed, rows, cols, block, spread=40):
+    g = np.random.default_rng(seed)
+    t = g.integers(-spread, spread, (rows, cols // block))
+    x = g.standard_normal((rows, cols)) * np.repeat(np.exp2(t), block, axis=1)
+    x[g.random((rows, cols)) < 0.01] = 0.0
+    x[g.random((rows, cols)) < 0.01] = -0.0
+    return x.astype(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("fmt,block", PACKED_CASES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+def test_packed_round_trip_equals_fake_quant(fmt, block, dtype):
+    """Decoding the stored codes and scales (table / E4M3 decode / 2^(b-127))
+    gives the fake-quantized tensor bit for bit, signed zeros included."""
+    x = _wide(block + len(fmt), 6, 48 * block, block)
+    if dtype == "f16":
+        x = np.clip(x, -6e4, 6e4)
+    xb = oracle.to_dtype_bits(x, dtype)
+    xv = oracle.from_dtype_bits(xb, dtype)
+    codes, scales = oracle.quantize_cache_packed(xv, fmt, block)
+    assert codes.shape == (6, 48 * block // (1 if fmt == "fp8" else 2)) and scales.shape == (6, 48)
+    assert codes.dtype == np.uint8 and scales.dtype == np.uint8
+    back = oracle.dequantize_cache_packed(codes, scales, fmt, block, dtype)
+    assert np.array_equal(back, oracle.quantize_cache(xv, fmt, block, dtype))
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4", "nvfp4"])
+def test_packed_scale_bytes_hold_the_ceiling(fmt):
+    """The stored scale is the smallest power of two s with amax <= s * fmax
+    (floored at 2^-126; nvfp4 clamped to 2^-9 .. 2^8), read back from its byte
+    independently: E8M0 as 2^(b-127), E4M3 through PyTorch's float8_e4m3fn."""
+    x = _wide(3, 16, 512, 32, spread=12 if fmt == "nvfp4" else 40)
+    codes, scales = oracle.quantize_cache_packed(x, fmt, 32)
+    if fmt == "nvfp4":
+        s = torch.from_numpy(scales).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    else:
+        s = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    fmax = FORMAT_FMAX[fmt]
+    amax = np.max(np.abs(x.reshape(16, 16, 32)), axis=-1)
+    m, _ = np.frexp(s)
+    assert np.all(m == 0.5)                                       # powers of two
+    lo, hi = (2.0 ** -9, 2.0 ** 8) if fmt == "nvfp4" else (2.0 ** -126, np.inf)
+    free = (s > lo) & (s < hi)
+    assert free.mean() > 0.5
+    assert np.all(amax[free] <= s[free] * fmax) and np.all(amax[free] > s[free] / 2 * fmax)
+    assert np.all(s >= lo) and np.all(s <= hi)
+
+
+def test_packed_fp8_codes_are_torchs_cast():
+    x = _wide(4, 32, 1024, 128)
+    codes, scales = oracle.quantize_cache_packed(x, "fp8", 128)
+    s = np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 128, axis=1)
+    want = torch.from_numpy((x / s).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, want)
+
+
+def test_packed_hand_block():
+    """amax 6 gives s = 1 (E8M0 127, E4M3 0x38): 6.0 -> code 7 and -0.5 -> code 9
+    share byte 0 (even channel low); -0.0 -> code 0; -0.1 rounds to a signed
+    zero, code 8, which decodes to +0.0.  fp8: amax 6 -> s = 2^-6 (byte 121)."""
+    x = np.zeros((1, 16))
+    x[0, :4] = [6.0, -0.5, -0.0, -0.1]
+    for fmt, sbyte in (("mxfp4", 127), ("nvfp4", 0x38)):
+        codes, scales = oracle.quantize_cache_packed(x, fmt, 16)
+        assert codes[0, 0] == 0x97 and codes[0, 1] == 0x80 and np.all(codes[0, 2:] == 0) and scales[0, 0] == sbyte
+        back = oracle.dequantize_cache_packed(codes, scales, fmt, 16, "f32")
+        assert back[0, 3] == 0 and not np.signbit(oracle.from_dtype_bits(back, "f32")[0, 3])
+    codes, scales = oracle.quantize_cache_packed(x, "fp8", 16)
+    # x / 2^-6: 384 = 1.5 * 2^8 (0x7C), -32 = -2^5 (0xE0), -0.0 (0x80), -6.4 -> -6.5 = -1.625 * 2^2 (0xCD)
+    assert scales[0, 0] == 121 and list(codes[0, :4]) == [0x7C, 0xE0, 0x80, 0xCD]
+
+
+def test_packed_bad_arguments():
+    with pytest.raises(ValueError):
+        oracle.quantize_cache_packed(np.zeros((2, 40)), "fp8", 32)     # partial group
+    with pytest.raises(ValueError):
+        oracle.quantize_cache_packed(np.zeros((2, 42)), "mxfp4", 7)    # odd fp4 group
+    with pytest.raises(ValueError):
+        oracle.quantize_cache_packed(np.zeros((2, 32)), "int4", 32)
