@@ -11,7 +11,8 @@ workload, all inputs already resident in HBM:
   gate/up grad_x (re-dequantizing the weights);
 * grouped GEMM forward, 8 experts, x [4096, 4096], W [8, 2048, 4096];
 * quantize_cache on a bf16 KV cache [4, 8192, 512]: fp8/128, mxfp4/32,
-  nvfp4/16, and the straight-through backward copy;
+  nvfp4/16, and the straight-through backward copy; the packed storage form
+  of each (codes + scale bytes) and its dequantize-on-read;
 * bulk bf16 [65536, 7168]: quantize_mxfp4, dequantize_mxfp4, quantize_cache
   nvfp4/16, fp8/128 and mxfp4/32; dequantization of a 2^30-parameter
   mxfp4 weight [64, 4096, 4096] to bf16;
@@ -197,6 +198,26 @@ def main():
             check(L.quantize_cache_bwd(kv_g[j].data_ptr(), kv_gi[j].data_ptr(), 1, n_kv, sp), "ste")
         legs.append(Leg("kv.ste_bwd", "k_copy16", "byte", 4.0 * n_kv, ste, reps=KV_REPS))
 
+        # packed KV storage: store codes + scale bytes, dequantize on read (same rotating inputs)
+        for fmt, code, block in [("fp8", 0, 128), ("mxfp4", 1, 32), ("nvfp4", 2, 16)]:
+            cb = 1.0 if fmt == "fp8" else 0.5
+            kv_c = [torch.empty(int(n_kv * cb), dtype=torch.uint8, device=dev) for _ in range(R)]
+            kv_s = [torch.empty(n_kv // block, dtype=torch.uint8, device=dev) for _ in range(R)]
+
+            def fq(i, code=code, block=block, kv_x=kv_xs[fmt], kv_c=kv_c, kv_s=kv_s):
+                j = i % R
+                check(L.quantize_cache_packed(kv_x[j].data_ptr(), 1, rows_kv, C_kv, code, block, kv_c[j].data_ptr(),
+                                              kv_s[j].data_ptr(), sp), "kv.pack")
+
+            def fd(i, code=code, block=block, kv_c=kv_c, kv_s=kv_s):
+                j = i % R
+                check(L.dequantize_cache_packed(kv_c[j].data_ptr(), kv_s[j].data_ptr(), rows_kv, C_kv, code, block,
+                                                kv_o[j].data_ptr(), 1, sp), "kv.unpack")
+            legs.append(Leg(f"kv.pack.{fmt}", f"k_quantize_cache_packed<bf16,{fmt},{block // 8}>", "byte",
+                            n_kv * (2 + cb + 1 / block), fq, reps=KV_REPS))
+            legs.append(Leg(f"kv.unpack.{fmt}", f"k_dequantize_cache_packed<bf16,{fmt},{block // 8}>", "byte",
+                            n_kv * (cb + 1 / block + 2), fd, reps=KV_REPS))
+
     # ---------------- bulk bf16 [65536, 7168] + 2^30-parameter weight dequant
     if wanted("bulk"):
         bulk = synth.bulk_stream(seed=0)
@@ -339,7 +360,7 @@ def main():
         "config": {
             "workload": "routed-expert layer share (32 experts, hidden 7168, intermediate 2048, 131072 routed rows, "
                         "fwd + grad_x) + 8-expert GEMM [4096x4096 -> 2048] + bf16 KV cache [4,8192,512] fake-quant "
-                        "fp8/128, mxfp4/32, nvfp4/16 + STE + bulk bf16 [65536,7168] codecs (mxfp4, two-level nvfp4, "
+                        "fp8/128, mxfp4/32, nvfp4/16 + STE + packed KV store/load + bulk bf16 [65536,7168] codecs (mxfp4, two-level nvfp4, "
                         "cache fake-quant) + [64,4096,4096] weight dequant + W4A4 routed-expert forwards",
             "value_is": "grouped-GEMM TFLOP/s of the routed-expert layer legs (event time)",
             "moe_rows": moe_rows,

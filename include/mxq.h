@@ -40,7 +40,7 @@ typedef enum {
   MXQ_ERR_SHAPE = -2,   /* negative size, K % 32 != 0, or inconsistent sizes    */
   MXQ_ERR_DTYPE = -3,   /* dtype code not supported by this entry point        */
   MXQ_ERR_FORMAT = -4,  /* format code not one of mxq_format                   */
-  MXQ_ERR_BLOCK = -5,   /* block_size <= 0                                     */
+  MXQ_ERR_BLOCK = -5,   /* block_size <= 0 (or odd for packed fp4 storage)     */
   MXQ_ERR_ALIGN = -6,   /* grouped GEMM activation / packed weights / output not 16-B aligned */
   MXQ_ERR_ALIAS = -7,   /* output overlaps an input that must stay unmodified  */
   MXQ_ERR_HIP = -8      /* a HIP launch reported an error                      */
@@ -102,6 +102,39 @@ int quantize_cache(const void* x, void* out, int t, int64_t rows, int64_t channe
  * rejected with MXQ_ERR_ALIAS.
  */
 int quantize_cache_bwd(const void* grad_out, void* grad_in, int t, int64_t numel, void* stream);
+
+/*
+ * quantize_cache_packed -- packed KV-cache storage: the codes and group scales
+ * that quantize_cache ([QC] quantize_cache, with the scale rule and element
+ * casts described there) rounds through, stored instead of multiplied back.
+ * x [rows, channels] of dtype t, whole groups only (channels % block_size ==
+ * 0; block_size even for mxfp4/nvfp4).  Writes
+ *   codes: mxfp4/nvfp4 uint8 [rows, channels/2], e2m1 codes two per byte, the
+ *          even channel in the low nibble, sign bit for x < 0 (-0.0 -> +0);
+ *          fp8 uint8 [rows, channels], E4M3 (FN) bytes, sign kept;
+ *   scales: uint8 [rows, channels/block_size], the group scale 2^k as an E8M0
+ *          byte k + 127 (mxfp4, fp8) or as E4M3 bits (nvfp4, k in -9..8).
+ * dequantize_cache_packed of the result equals quantize_cache of x bit for
+ * bit.  Fast path: block_size a power of two in [8, 512], x 16-byte aligned,
+ * codes 4-byte (fp4) or 8-byte (fp8) aligned; anything else runs one thread
+ * per group.  Inputs must be finite.  Buffers are the caller's (device
+ * memory); none may overlap.
+ * Errors: MXQ_ERR_SHAPE (negative sizes, channels % block_size != 0),
+ * MXQ_ERR_DTYPE, MXQ_ERR_FORMAT, MXQ_ERR_BLOCK (block_size <= 0, or odd for
+ * the fp4 formats), MXQ_ERR_NULL, MXQ_ERR_ALIAS, MXQ_ERR_HIP.
+ */
+int quantize_cache_packed(const void* x, int t, int64_t rows, int64_t channels, int fmt, int32_t block_size,
+                          uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * dequantize_cache_packed -- dequant-on-read of the packed form: out[i] =
+ * code value (e2m1 table, code 8 -> +0.0; or E4M3) times the group's scale
+ * (2^(b-127) for an E8M0 byte, the E4M3 value for nvfp4; NaN bytes give NaN),
+ * rounded nearest-even to t, into out [rows, channels].  Same layouts, checks
+ * and errors as quantize_cache_packed (fast path: out 16-byte aligned).
+ */
+int dequantize_cache_packed(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t channels, int fmt,
+                            int32_t block_size, void* out, int t, void* stream);
 
 /*
  * quantize_nvfp4 -- [MO] section "NVFP4 in the code: two scales and a

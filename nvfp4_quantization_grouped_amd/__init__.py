@@ -20,6 +20,8 @@ from .ops import (
     quantize_cache,
     quantize_cache_bwd,
     quantize_cache_forward,
+    quantize_cache_packed,
+    dequantize_cache_packed,
     quantize_mxfp4,
     quantize_nvfp4,
 )
@@ -30,5 +32,5 @@ __all__ = [
     "dequantize_mxfp4", "mxfp4_grouped_mm_bwd_x", "mxfp4_grouped_mm_fwd",
     "mxfp4_grouped_mm_fwd_w4a4", "mxfp4_grouped_mm_fwd_w4a4_quantized",
     "quantize_cache", "quantize_cache_bwd", "quantize_cache_forward", "quantize_mxfp4",
-    "quantize_nvfp4", "dequantize_nvfp4",
+    "quantize_nvfp4", "dequantize_nvfp4", "quantize_cache_packed", "dequantize_cache_packed",
 ]

@@ -68,6 +68,46 @@ int quantize_cache_bwd(const void* grad_out, void* grad_in, int t, int64_t numel
   return from_hip(mxq::launch_copy(grad_out, grad_in, bytes, (hipStream_t)stream));
 }
 
+// Shared argument checks of the packed cache entries; sets the code and scale byte counts.
+static int cache_packed_check(int t, int64_t rows, int64_t channels, int fmt, int32_t block, int64_t* ncode,
+                              int64_t* nscale) {
+  if (rows < 0 || channels < 0) return MXQ_ERR_SHAPE;
+  if (!dtype_ok(t)) return MXQ_ERR_DTYPE;
+  if (fmt != MXQ_FMT_FP8 && fmt != MXQ_FMT_MXFP4 && fmt != MXQ_FMT_NVFP4) return MXQ_ERR_FORMAT;
+  if (block <= 0 || (fmt != MXQ_FMT_FP8 && block % 2 != 0)) return MXQ_ERR_BLOCK;
+  if (channels % block != 0) return MXQ_ERR_SHAPE;
+  const int64_t n = rows * channels;
+  *ncode = fmt == MXQ_FMT_FP8 ? n : n / 2;
+  *nscale = n / block;
+  return MXQ_OK;
+}
+
+int quantize_cache_packed(const void* x, int t, int64_t rows, int64_t channels, int fmt, int32_t block_size,
+                          uint8_t* codes, uint8_t* scales, void* stream) {
+  int64_t nc = 0, ns = 0;
+  const int st = cache_packed_check(t, rows, channels, fmt, block_size, &nc, &ns);
+  if (st != MXQ_OK) return st;
+  if (rows == 0 || channels == 0) return MXQ_OK;
+  if (!x || !codes || !scales) return MXQ_ERR_NULL;
+  const int64_t xb = rows * channels * dtype_bytes(t);
+  if (overlap(x, xb, codes, nc) || overlap(x, xb, scales, ns) || overlap(codes, nc, scales, ns)) return MXQ_ERR_ALIAS;
+  return from_hip(
+      mxq::launch_quantize_cache_packed(x, t, rows, channels, fmt, block_size, codes, scales, (hipStream_t)stream));
+}
+
+int dequantize_cache_packed(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t channels, int fmt,
+                            int32_t block_size, void* out, int t, void* stream) {
+  int64_t nc = 0, ns = 0;
+  const int st = cache_packed_check(t, rows, channels, fmt, block_size, &nc, &ns);
+  if (st != MXQ_OK) return st;
+  if (rows == 0 || channels == 0) return MXQ_OK;
+  if (!codes || !scales || !out) return MXQ_ERR_NULL;
+  const int64_t ob = rows * channels * dtype_bytes(t);
+  if (overlap(out, ob, codes, nc) || overlap(out, ob, scales, ns)) return MXQ_ERR_ALIAS;
+  return from_hip(mxq::launch_dequantize_cache_packed(codes, scales, rows, channels, fmt, block_size, out, t,
+                                                      (hipStream_t)stream));
+}
+
 int quantize_nvfp4(const void* x, int xt, int64_t rows, int64_t k, uint8_t* packed, uint8_t* block_scales,
                    float* global_scale, void* stream) {
   if (rows < 0 || k < 0 || k % 16 != 0) return MXQ_ERR_SHAPE;

@@ -1,4 +1,5 @@
-// Streaming codec kernels: quantize_mxfp4, dequantize_mxfp4, quantize_cache
+// Streaming codec kernels: quantize_mxfp4, dequantize_mxfp4, quantize_cache,
+// its packed storage form,
 // and the straight-through copy.  All are HBM-bound streams.
 //
 // Fast path: a lane owns a "chunk" of 8 consecutive elements (one 16-byte
@@ -150,18 +151,13 @@ __device__ __forceinline__ void decode_fp4_chunk(uint32_t c, float s, Chunk<DT>&
   }
 }
 
-// Eight elements -> E4M3 -> eight values of DT, scale s (nearest-even both ways).
+// Eight elements -> eight E4M3 codes of x / s, nearest-even, sign kept (c0 holds
+// elements 0..3, c1 elements 4..7, element i in byte i of the pair).
 template <int DT>
-__device__ __forceinline__ void fake_quant_fp8_chunk(const Chunk<DT>& in, float s, Chunk<DT>& out) {
+__device__ __forceinline__ void encode_fp8_chunk(const Chunk<DT>& in, float s, uint32_t& c0, uint32_t& c1) {
   if constexpr (DT == DT_BF16) {
-    uint32_t c0 = enc_fp8_bf16x2<false>(0u, in.w[0], s);
-    c0 = enc_fp8_bf16x2<true>(c0, in.w[1], s);
-    uint32_t c1 = enc_fp8_bf16x2<false>(0u, in.w[2], s);
-    c1 = enc_fp8_bf16x2<true>(c1, in.w[3], s);
-    out.w[0] = dec_fp8_bf16x2<false>(c0, s);
-    out.w[1] = dec_fp8_bf16x2<true>(c0, s);
-    out.w[2] = dec_fp8_bf16x2<false>(c1, s);
-    out.w[3] = dec_fp8_bf16x2<true>(c1, s);
+    c0 = enc_fp8_bf16x2<true>(enc_fp8_bf16x2<false>(0u, in.w[0], s), in.w[1], s);
+    c1 = enc_fp8_bf16x2<true>(enc_fp8_bf16x2<false>(0u, in.w[2], s), in.w[3], s);
   } else {
     float v[8];
     if constexpr (DT == DT_F32) {
@@ -171,12 +167,26 @@ __device__ __forceinline__ void fake_quant_fp8_chunk(const Chunk<DT>& in, float 
 #pragma unroll
       for (int i = 0; i < 4; ++i) { v[2 * i] = f16_lo(in.w[i]); v[2 * i + 1] = f16_hi(in.w[i]); }
     }
+    c0 = enc_fp8_f2<true>(enc_fp8_f2<false>(0u, v[0], v[1], s), v[2], v[3], s);
+    c1 = enc_fp8_f2<true>(enc_fp8_f2<false>(0u, v[4], v[5], s), v[6], v[7], s);
+  }
+}
+
+// Eight E4M3 codes -> eight values of DT: code value times s, rounded
+// nearest-even to DT (exact in fp32, then one rounding for f16).
+template <int DT>
+__device__ __forceinline__ void decode_fp8_chunk(uint32_t c0, uint32_t c1, float s, Chunk<DT>& out) {
+  if constexpr (DT == DT_BF16) {
+    out.w[0] = dec_fp8_bf16x2<false>(c0, s);
+    out.w[1] = dec_fp8_bf16x2<true>(c0, s);
+    out.w[2] = dec_fp8_bf16x2<false>(c1, s);
+    out.w[3] = dec_fp8_bf16x2<true>(c1, s);
+  } else {
     float o[8];
+    const uint32_t c[2] = {c0, c1};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      uint32_t c = enc_fp8_f2<false>(0u, v[4 * h], v[4 * h + 1], s);
-      c = enc_fp8_f2<true>(c, v[4 * h + 2], v[4 * h + 3], s);
-      f32x2_t a = dec_fp8_f2<false>(c, s), b = dec_fp8_f2<true>(c, s);
+      f32x2_t a = dec_fp8_f2<false>(c[h], s), b = dec_fp8_f2<true>(c[h], s);
       o[4 * h] = a.x; o[4 * h + 1] = a.y; o[4 * h + 2] = b.x; o[4 * h + 3] = b.y;
     }
     if constexpr (DT == DT_F32) {
@@ -187,6 +197,14 @@ __device__ __forceinline__ void fake_quant_fp8_chunk(const Chunk<DT>& in, float 
       for (int i = 0; i < 4; ++i) out.w[i] = pack_f16x2(o[2 * i], o[2 * i + 1]);
     }
   }
+}
+
+// Eight elements -> E4M3 -> eight values of DT, scale s (nearest-even both ways).
+template <int DT>
+__device__ __forceinline__ void fake_quant_fp8_chunk(const Chunk<DT>& in, float s, Chunk<DT>& out) {
+  uint32_t c0, c1;
+  encode_fp8_chunk<DT>(in, s, c0, c1);
+  decode_fp8_chunk<DT>(c0, c1, s, out);
 }
 
 // ------------------------------------------------------------- quantize_mxfp4
@@ -670,6 +688,156 @@ __global__ void __launch_bounds__(kThreads) k_dequantize_nvfp4_general(const uin
   }
 }
 
+// ------------------------------------------------- packed KV-cache storage
+// The codes and group scales quantize_cache rounds through, stored: e2m1
+// nibbles (even channel low, sign bit for x < 0) or E4M3 bytes, and one scale
+// byte per group.  The element arithmetic is quantize_cache's, so decoding
+// the stored form gives the fake-quantized values bit for bit.
+
+// Scale byte of 2^k: E8M0 (k + 127) for mxfp4 and fp8; E4M3 bits for nvfp4,
+// whose k is in [-9, 8] (normal for k >= -6, else the subnormal 2^(k+9) * 2^-9).
+template <int FMT>
+__device__ __forceinline__ uint32_t cache_scale_byte(int k) {
+  if constexpr (FMT == FMT_NVFP4) return k >= -6 ? (uint32_t)(k + 7) << 3 : 1u << (k + 9);
+  else return (uint32_t)(k + 127);
+}
+// Scale byte -> fp32 scale.  The scaled conversions use only the exponent of
+// their scale operand, which is exact for E8M0 but not for an E4M3 byte with
+// mantissa bits, so nvfp4 decodes at scale 1 and multiplies in fp32 (e2m1
+// times E4M3 is exact in fp32, bf16 and f16).
+template <int FMT>
+__device__ __forceinline__ float cache_scale_value(uint32_t b) {
+  if constexpr (FMT == FMT_NVFP4) return dec_fp8_f2<false>(b, 1.0f).x;   // E4M3 decode; 0x7F/0xFF -> NaN
+  else return e8m0_to_f32(b);
+}
+
+// Fast path: lane = chunk of 8 elements, group = L consecutive lanes (block 8L).
+template <int DT, int FMT, int L, class M>
+__global__ void __launch_bounds__(kThreads) k_quantize_cache_packed(const uint8_t* __restrict__ x,
+                                                                  uint8_t* __restrict__ codes,
+                                                                  uint8_t* __restrict__ scales, int64_t nchunks) {
+  const int64_t step = (int64_t)gridDim.x * kThreads * M::kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * M::kUnroll; base < nchunks; base += step) {
+    Chunk<DT> ch[M::kUnroll];
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u) {
+      const int64_t c = base + u * kThreads + threadIdx.x;
+      if (c < nchunks) load_chunk<DT, M>(x, c, ch[u]);
+      else {
+#pragma unroll
+        for (int i = 0; i < Chunk<DT>::kWords; ++i) ch[u].w[i] = 0u;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u) {
+      const int64_t c = base + u * kThreads + threadIdx.x;
+      const uint32_t amax = group_max_u32<L>(chunk_amax_bits<DT>(ch[u]));
+      const int k = ceil_rule_exponent<FMT>(amax);
+      const float s = pow2f(k);
+      if constexpr (FMT == FMT_FP8) {
+        uint32_t c0, c1;
+        encode_fp8_chunk<DT>(ch[u], s, c0, c1);
+        if (c < nchunks) M::st(u32x2_t{c0, c1}, reinterpret_cast<u32x2_t*>(codes) + c);
+      } else {
+        const uint32_t w = encode_fp4_chunk<DT, true>(ch[u], s);
+        if (c < nchunks) M::st(w, reinterpret_cast<uint32_t*>(codes) + c);
+      }
+      if (c < nchunks && (c & (L - 1)) == 0) scales[c / L] = (uint8_t)cache_scale_byte<FMT>(k);
+    }
+  }
+}
+
+template <int DT, int FMT, int L, class M>
+__global__ void __launch_bounds__(kThreads) k_dequantize_cache_packed(const uint8_t* __restrict__ codes,
+                                                                    const uint8_t* __restrict__ scales,
+                                                                    uint8_t* __restrict__ out, int64_t nchunks) {
+  const int64_t step = (int64_t)gridDim.x * kThreads * M::kUnroll;
+  for (int64_t base = (int64_t)blockIdx.x * kThreads * M::kUnroll; base < nchunks; base += step) {
+    u32x2_t cw[M::kUnroll];
+    uint32_t sb[M::kUnroll];
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u) {
+      const int64_t c = base + u * kThreads + threadIdx.x;
+      if constexpr (FMT == FMT_FP8) cw[u] = c < nchunks ? M::ld(reinterpret_cast<const u32x2_t*>(codes) + c) : u32x2_t{0u, 0u};
+      else cw[u].x = c < nchunks ? M::ld(reinterpret_cast<const uint32_t*>(codes) + c) : 0u;
+      sb[u] = c < nchunks ? (uint32_t)scales[c / L] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u) {
+      const int64_t c = base + u * kThreads + threadIdx.x;
+      const float s = cache_scale_value<FMT>(sb[u]);
+      Chunk<DT> o;
+      if constexpr (FMT == FMT_FP8) decode_fp8_chunk<DT>(cw[u].x, cw[u].y, s, o);
+      else if constexpr (FMT == FMT_NVFP4) nvfp4_decode_chunk<DT>(clear_negzero_codes(cw[u].x), s, o);
+      else decode_fp4_chunk<DT>(clear_negzero_codes(cw[u].x), s, o);
+      if (c < nchunks) store_chunk<DT, M>(out, c, o);
+    }
+  }
+}
+
+// General path: one thread per group (whole groups of any size, even for the
+// fp4 formats; any alignment).
+template <int DT, int FMT>
+__global__ void __launch_bounds__(kThreads) k_quantize_cache_packed_general(const uint8_t* __restrict__ x,
+                                                                          uint8_t* __restrict__ codes,
+                                                                          uint8_t* __restrict__ scales,
+                                                                          int64_t groups, int64_t block) {
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < groups; g += (int64_t)gridDim.x * kThreads) {
+    const int64_t o0 = g * block;
+    uint32_t amax = 0;
+    for (int64_t i = 0; i < block; ++i) amax = max(amax, as_u32(load_elem<DT>(x, o0 + i)) & 0x7FFFFFFFu);
+    const int k = ceil_rule_exponent<FMT>(amax);
+    const float s = pow2f(k);
+    if constexpr (FMT == FMT_FP8) {
+      for (int64_t i = 0; i < block; ++i)
+        codes[o0 + i] = (uint8_t)(enc_fp8_f2<false>(0u, load_elem<DT>(x, o0 + i), 0.0f, s) & 0xFFu);
+    } else {
+      for (int64_t j = 0; j < block / 2; ++j) {
+        const float a = load_elem<DT>(x, o0 + 2 * j) + 0.0f, b = load_elem<DT>(x, o0 + 2 * j + 1) + 0.0f;
+        codes[o0 / 2 + j] = (uint8_t)(enc_fp4_f2<0>(0u, a, b, s) & 0xFFu);
+      }
+    }
+    scales[g] = (uint8_t)cache_scale_byte<FMT>(k);
+  }
+}
+
+template <int DT, int FMT>
+__global__ void __launch_bounds__(kThreads) k_dequantize_cache_packed_general(const uint8_t* __restrict__ codes,
+                                                                            const uint8_t* __restrict__ scales,
+                                                                            uint8_t* __restrict__ out,
+                                                                            int64_t groups, int64_t block) {
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < groups; g += (int64_t)gridDim.x * kThreads) {
+    const int64_t o0 = g * block;
+    const float s = cache_scale_value<FMT>(scales[g]);
+    if constexpr (FMT == FMT_FP8) {
+      for (int64_t i = 0; i < block; ++i) {
+        const uint32_t code = codes[o0 + i];
+        const float v = dec_fp8_f2<false>(code, s).x;
+        store_elem<DT>(out, o0 + i, v, DT == DT_BF16 ? dec_fp8_bf16x2<false>(code, s) & 0xFFFFu : 0u);
+      }
+    } else {
+      for (int64_t j = 0; j < block / 2; ++j) {
+        const uint32_t code = clear_negzero_codes((uint32_t)codes[o0 / 2 + j]);
+        if constexpr (FMT == FMT_NVFP4) {
+          const uint32_t h = dec_fp4_bf16x2<0>(code, 1.0f);
+          const float v0 = mul_f32(bf16_lo(h), s), v1 = mul_f32(bf16_hi(h), s);
+          const uint32_t bb = pack_bf16x2_rne(v0, v1);
+          store_elem<DT>(out, o0 + 2 * j, v0, bb & 0xFFFFu);
+          store_elem<DT>(out, o0 + 2 * j + 1, v1, bb >> 16);
+        } else if constexpr (DT == DT_F16) {
+          const uint32_t h = dec_fp4_f16x2<0>(code, s);
+          *reinterpret_cast<unsigned short*>(out + 2 * (o0 + 2 * j)) = (unsigned short)(h & 0xFFFFu);
+          *reinterpret_cast<unsigned short*>(out + 2 * (o0 + 2 * j + 1)) = (unsigned short)(h >> 16);
+        } else {
+          const uint32_t h = dec_fp4_bf16x2<0>(code, s);
+          store_elem<DT>(out, o0 + 2 * j, as_f32(h << 16), h & 0xFFFFu);
+          store_elem<DT>(out, o0 + 2 * j + 1, as_f32(h & 0xFFFF0000u), h >> 16);
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ launchers
 static inline int grid_for(int64_t items, int64_t per_block) {
   const int64_t cap = kGridCap;
@@ -793,6 +961,102 @@ hipError_t launch_quantize_cache(const void* x, void* out, int dt, int64_t rows,
     case DT_BF16: return launch_quantize_cache_dt<DT_BF16>(x, out, rows, channels, fmt, block, st);
     default: return launch_quantize_cache_dt<DT_F16>(x, out, rows, channels, fmt, block, st);
   }
+}
+
+// Packed cache storage.  Fast path: block a power of two in [8, 512], 16-byte
+// aligned x / out and codes aligned to one chunk's codes (4 or 8 bytes).
+template <int FMT>
+static bool packed_fast(int32_t block, const void* elems, const void* codes) {
+  const bool pow2 = block >= 8 && block <= 512 && (block & (block - 1)) == 0;
+  return pow2 && aligned(elems, 16) && aligned(codes, FMT == FMT_FP8 ? 8 : 4);
+}
+
+template <int DT, int FMT, int L>
+static void launch_packed_q(const void* x, uint8_t* codes, uint8_t* scales, int64_t nchunks, hipStream_t st) {
+  const int64_t bytes = nchunks * 8 * (DT == DT_F32 ? 4 : 2);
+  const uint8_t* xp = (const uint8_t*)x;
+  if (bytes >= kBigStreamBytes)
+    hipLaunchKernelGGL((k_quantize_cache_packed<DT, FMT, L, StreamBig>),
+                       dim3(grid_for(nchunks, kThreads * StreamBig::kUnroll)), dim3(kThreads), 0, st, xp, codes, scales,
+                       nchunks);
+  else if (bytes >= kTinyStreamBytes)
+    hipLaunchKernelGGL((k_quantize_cache_packed<DT, FMT, L, StreamSmall>),
+                       dim3(grid_for(nchunks, kThreads * StreamSmall::kUnroll)), dim3(kThreads), 0, st, xp, codes,
+                       scales, nchunks);
+  else
+    hipLaunchKernelGGL((k_quantize_cache_packed<DT, FMT, L, StreamTiny>),
+                       dim3(grid_for(nchunks, kThreads * StreamTiny::kUnroll)), dim3(kThreads), 0, st, xp, codes,
+                       scales, nchunks);
+}
+
+template <int DT, int FMT, int L>
+static void launch_packed_dq(const uint8_t* codes, const uint8_t* scales, void* out, int64_t nchunks,
+                             hipStream_t st) {
+  hipLaunchKernelGGL((k_dequantize_cache_packed<DT, FMT, L, StreamDequant>),
+                     dim3(grid_for(nchunks, kThreads * StreamDequant::kUnroll)), dim3(kThreads), 0, st, codes, scales,
+                     (uint8_t*)out, nchunks);
+}
+
+template <int DT, int FMT>
+static hipError_t launch_cache_packed_t(bool dequant, const void* x, uint8_t* codes, const uint8_t* scales_in,
+                                        uint8_t* scales_out, void* out, int64_t n, int32_t block, hipStream_t st) {
+  if (packed_fast<FMT>(block, dequant ? out : x, codes)) {
+    const int64_t nc = n / 8;
+#define MXQ_PACKED_CASE(B, L)                                                        \
+  case B:                                                                            \
+    if (dequant) launch_packed_dq<DT, FMT, L>(codes, scales_in, out, nc, st);       \
+    else launch_packed_q<DT, FMT, L>(x, codes, scales_out, nc, st);                 \
+    break;
+    switch (block) {
+      MXQ_PACKED_CASE(8, 1)
+      MXQ_PACKED_CASE(16, 2)
+      MXQ_PACKED_CASE(32, 4)
+      MXQ_PACKED_CASE(64, 8)
+      MXQ_PACKED_CASE(128, 16)
+      MXQ_PACKED_CASE(256, 32)
+      default: MXQ_PACKED_CASE(512, 64)
+    }
+#undef MXQ_PACKED_CASE
+  } else {
+    const int64_t groups = n / block;
+    if (dequant)
+      hipLaunchKernelGGL((k_dequantize_cache_packed_general<DT, FMT>), dim3(grid_for(groups, kThreads)), dim3(kThreads),
+                         0, st, codes, scales_in, (uint8_t*)out, groups, (int64_t)block);
+    else
+      hipLaunchKernelGGL((k_quantize_cache_packed_general<DT, FMT>), dim3(grid_for(groups, kThreads)), dim3(kThreads),
+                         0, st, (const uint8_t*)x, codes, scales_out, groups, (int64_t)block);
+  }
+  return hipGetLastError();
+}
+
+template <int DT>
+static hipError_t launch_cache_packed_dt(bool dequant, const void* x, uint8_t* codes, const uint8_t* si, uint8_t* so,
+                                         void* out, int64_t n, int fmt, int32_t block, hipStream_t st) {
+  switch (fmt) {
+    case FMT_FP8: return launch_cache_packed_t<DT, FMT_FP8>(dequant, x, codes, si, so, out, n, block, st);
+    case FMT_MXFP4: return launch_cache_packed_t<DT, FMT_MXFP4>(dequant, x, codes, si, so, out, n, block, st);
+    default: return launch_cache_packed_t<DT, FMT_NVFP4>(dequant, x, codes, si, so, out, n, block, st);
+  }
+}
+
+static hipError_t launch_cache_packed(bool dequant, const void* x, uint8_t* codes, const uint8_t* si, uint8_t* so,
+                                      void* out, int dt, int64_t n, int fmt, int32_t block, hipStream_t st) {
+  switch (dt) {
+    case DT_F32: return launch_cache_packed_dt<DT_F32>(dequant, x, codes, si, so, out, n, fmt, block, st);
+    case DT_BF16: return launch_cache_packed_dt<DT_BF16>(dequant, x, codes, si, so, out, n, fmt, block, st);
+    default: return launch_cache_packed_dt<DT_F16>(dequant, x, codes, si, so, out, n, fmt, block, st);
+  }
+}
+
+hipError_t launch_quantize_cache_packed(const void* x, int dt, int64_t rows, int64_t channels, int fmt, int32_t block,
+                                        uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  return launch_cache_packed(false, x, codes, nullptr, scales, nullptr, dt, rows * channels, fmt, block, st);
+}
+
+hipError_t launch_dequantize_cache_packed(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t channels,
+                                          int fmt, int32_t block, void* out, int dt, hipStream_t st) {
+  return launch_cache_packed(true, nullptr, const_cast<uint8_t*>(codes), scales, nullptr, out, dt, rows * channels,
+                             fmt, block, st);
 }
 
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st) {

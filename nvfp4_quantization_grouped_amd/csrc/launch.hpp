@@ -19,6 +19,11 @@ hipError_t launch_quantize_nvfp4(const void* x, int dt, int64_t rows, int64_t k,
                                  float* global_scale, hipStream_t st);
 hipError_t launch_dequantize_nvfp4(const uint8_t* packed, const uint8_t* scales, const float* global_scale,
                                    int64_t rows, int64_t k, void* out, int dt, hipStream_t st);
+// Packed cache storage: codes [n] (fp8) or [n/2] (e2m1), one scale byte per group; whole groups only.
+hipError_t launch_quantize_cache_packed(const void* x, int dt, int64_t rows, int64_t channels, int fmt, int32_t block,
+                                        uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_dequantize_cache_packed(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t channels,
+                                          int fmt, int32_t block, void* out, int dt, hipStream_t st);
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
 hipError_t launch_zero(void* dst, int64_t bytes, hipStream_t st);
 // bwd = false: out[T, N] = a[T, K] W_e^T;  bwd = true: out[T, K] = a[T, N] W_e.

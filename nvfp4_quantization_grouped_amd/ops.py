@@ -176,6 +176,56 @@ def quantize_cache_bwd(grad_out, grad_in=None):
     return out
 
 
+def quantize_cache_packed(values, format, block_size):
+    """Packed KV-cache storage of ``values`` [..., channels] (whole groups):
+    returns (codes uint8 [..., channels/2] for mxfp4/nvfp4 or [..., channels]
+    for fp8, scales uint8 [..., channels/block_size]); the stored form of
+    quantize_cache's round trip."""
+    _need_cuda(values)
+    if values.dtype not in _DT:
+        raise TypeError(f"quantize_cache_packed: unsupported dtype {values.dtype}")
+    if format not in _FMT:
+        raise ValueError("quantize_cache_packed: format must be 'fp8', 'mxfp4' or 'nvfp4'")
+    x = values.contiguous()
+    if x.dim() == 0:
+        raise ValueError("quantize_cache_packed: needs at least one dimension")
+    C, B = x.shape[-1], int(block_size)
+    if B <= 0 or C % B or (format != "fp8" and B % 2):
+        raise ValueError("quantize_cache_packed: channels must be whole groups (an even block for the fp4 formats)")
+    rows = x.numel() // C if C else 0
+    codes = torch.empty(x.shape[:-1] + (C if format == "fp8" else C // 2,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1] + (C // B,), dtype=torch.uint8, device=x.device)
+    with torch.cuda.device(x.device):
+        st = _lib.lib().quantize_cache_packed(_ptr(x), _DT[x.dtype], rows, C, _FMT[format], B, _ptr(codes),
+                                              _ptr(scales), _stream(x.device))
+    _lib.check(st, "quantize_cache_packed")
+    return codes, scales
+
+
+def dequantize_cache_packed(codes, scales, format, block_size, dtype):
+    """Dequant-on-read of the packed form into a new ``dtype`` tensor [..., channels]."""
+    _need_cuda(codes, scales)
+    if dtype not in _DT:
+        raise TypeError(f"dequantize_cache_packed: unsupported dtype {dtype}")
+    if format not in _FMT:
+        raise ValueError("dequantize_cache_packed: format must be 'fp8', 'mxfp4' or 'nvfp4'")
+    c = codes.contiguous()
+    s = _as_u8(scales).contiguous()
+    if c.dtype != torch.uint8 or c.dim() == 0:
+        raise TypeError("dequantize_cache_packed: codes must be a uint8 tensor")
+    C = c.shape[-1] * (1 if format == "fp8" else 2)
+    B = int(block_size)
+    if B <= 0 or C % B or s.shape != c.shape[:-1] + (C // B,):
+        raise ValueError("dequantize_cache_packed: scales must be [..., channels / block_size]")
+    rows = c.numel() // c.shape[-1] if c.shape[-1] else 0
+    out = torch.empty(c.shape[:-1] + (C,), dtype=dtype, device=c.device)
+    with torch.cuda.device(c.device):
+        st = _lib.lib().dequantize_cache_packed(_ptr(c), _ptr(s), rows, C, _FMT[format], B, _ptr(out), _DT[dtype],
+                                                _stream(c.device))
+    _lib.check(st, "dequantize_cache_packed")
+    return out
+
+
 class CacheQuantization(torch.autograd.Function):
     """``_CacheQuantization``: quantize/dequantize in forward, pass the
     gradient through unchanged in backward (no gradient for block_size and

@@ -151,3 +151,28 @@ def test_ops_reject_cpu_tensors():
         mxq.quantize_mxfp4(torch.zeros(2, 32))
     with pytest.raises(ValueError):
         mxq.quantize_cache(torch.zeros(2, 32, dtype=torch.bfloat16), "fp8", 32)
+
+
+def test_cache_packed_validation(L):
+    q = L.quantize_cache_packed
+    # (x, dtype, rows, channels, fmt, block, codes, scales, stream)
+    assert q(FAKE, 1, 4, 40, 1, 32, FAKE * 2, FAKE * 3, None) == -2        # partial group
+    assert q(FAKE, 1, -1, 64, 1, 32, FAKE * 2, FAKE * 3, None) == -2
+    assert q(FAKE, 5, 4, 64, 1, 32, FAKE * 2, FAKE * 3, None) == -3        # dtype
+    assert q(FAKE, 1, 4, 64, 3, 32, FAKE * 2, FAKE * 3, None) == -4        # format
+    assert q(FAKE, 1, 4, 63, 1, 7, FAKE * 2, FAKE * 3, None) == -5         # odd fp4 group
+    assert q(FAKE, 1, 4, 63, 0, 7, None, FAKE * 3, None) == -1             # an odd fp8 group passes the block check
+    assert q(FAKE, 1, 4, 64, 1, 0, FAKE * 2, FAKE * 3, None) == -5
+    assert q(FAKE, 1, 4, 64, 2, 16, None, FAKE * 3, None) == -1
+    assert q(FAKE, 1, 4, 64, 0, 16, FAKE + 64, FAKE * 3, None) == -7       # codes inside x
+    assert q(FAKE, 1, 4, 64, 0, 16, FAKE * 2, FAKE * 2 + 255, None) == -7  # scales inside the fp8 codes
+    assert q(FAKE, 1, 0, 64, 1, 32, FAKE * 2, FAKE * 3, None) == 0         # nothing to do
+    d = L.dequantize_cache_packed
+    # (codes, scales, rows, channels, fmt, block, out, dtype, stream)
+    assert d(FAKE, FAKE * 2, 4, 40, 1, 32, FAKE * 3, 1, None) == -2
+    assert d(FAKE, FAKE * 2, 4, 64, 1, 32, FAKE * 3, 4, None) == -3
+    assert d(FAKE, FAKE * 2, 4, 64, -1, 32, FAKE * 3, 1, None) == -4
+    assert d(FAKE, FAKE * 2, 4, 66, 2, 11, FAKE * 3, 1, None) == -5
+    assert d(FAKE, None, 4, 64, 1, 32, FAKE * 3, 1, None) == -1
+    assert d(FAKE, FAKE * 2, 4, 64, 1, 32, FAKE - 100, 1, None) == -7      # out over the codes
+    assert d(FAKE, FAKE * 2, 0, 64, 1, 32, FAKE * 3, 1, None) == 0
