@@ -21,7 +21,8 @@ Sources (page title, then the section on that page):
 * "NVIDIA Model Optimizer: from mtq.quantize to a 4.95-bit DeepSeek-R1":
   section "NVFP4 in the code: two scales and a nibble" (tie rule of the e2m1
   cast, the E4M3 range 448 and smallest scale 2^-9, packing expression, and
-  the two-level NVFP4 format of ``oracle/nvfp4.py``); section "The claims,
+  the two-level NVFP4 format of ``oracle/nvfp4.py``); section "Where the
+  scales come from" (the MSE block-scale sweep); section "The claims,
   marked reported" (W4A4).
 
 Every function is pinned by tests under ``tests/test_oracle_*.py`` against facts
@@ -46,7 +47,8 @@ from .mxfp4 import quantize_mxfp4, dequantize_mxfp4, floor_scale_exponent
 from .cache import (power_of_two_ceiling, cache_scale, quantize_cache, quantize_cache_backward, quantize_cache_packed,
                     dequantize_cache_packed)
 from .nvfp4 import (global_scale as nvfp4_global_scale, e4m3_bits, e4m3_decode, encode_with_global_scale as nvfp4_encode,
-                    quantize_nvfp4, dequantize_nvfp4_values, dequantize_nvfp4)
+                    quantize_nvfp4, dequantize_nvfp4_values, dequantize_nvfp4, block_sq_errors as nvfp4_block_sq_errors,
+                    mse_block_scales as nvfp4_mse_block_scales, quantize_nvfp4_mse)
 from .grouped_mm import (dequantize_expert_weights, grouped_mm_fwd, grouped_mm_bwd_x, grouped_mm_rows, segments,
                          w4a4_activations, grouped_mm_fwd_w4a4)
 
@@ -60,5 +62,5 @@ __all__ = [
     "dequantize_expert_weights", "grouped_mm_fwd", "grouped_mm_bwd_x", "grouped_mm_rows", "segments",
     "w4a4_activations", "grouped_mm_fwd_w4a4",
     "nvfp4_global_scale", "e4m3_bits", "e4m3_decode", "nvfp4_encode", "quantize_nvfp4", "dequantize_nvfp4_values",
-    "dequantize_nvfp4",
+    "dequantize_nvfp4", "nvfp4_block_sq_errors", "nvfp4_mse_block_scales", "quantize_nvfp4_mse",
 ]

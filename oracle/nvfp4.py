@@ -25,6 +25,23 @@ Readings (the page gives the formulas, not the arithmetic):
 * A tensor whose max |x| is 0 has g = 0, where the formula would divide by
   zero: every block scale is then 1.0 (the zero-scale rule) and every code 0.
   *Parity unpinned by the page*; the kernels take the same reading.
+
+The MSE block-scale rule (same page, section "Where the scales come from",
+the paragraph on NVFP4's own rules): instead of the
+max rule, each block tries every positive finite E4M3 value (codes 0x01 ..
+0x7E, 126 of them) as s_b and keeps the one whose quantized block has the
+least squared error against x.  Readings:
+
+* g is the max rule's global scale; for each candidate the codes and the
+  dequantized values are the two-level ones above (d = fl(s g), codes of
+  fl(x / d), x_hat = fl(e2m1 * d)).
+* The error is computed in fp32 in a fixed order: e_i = fl(x_i - x_hat_i),
+  fl(e_i * e_i), summed i = 0 .. 15 left to right, each sum rounded (no
+  fused multiply-add).  The candidate chosen is the first, in increasing
+  code order, with an error strictly below every earlier one; candidates
+  whose d underflows to 0 are skipped.  An all-zero block therefore gets
+  code 0x01 (every candidate is exact), and g = 0 gives the max rule's
+  result (scales 1.0, codes 0).
 """
 
 import numpy as np
@@ -67,6 +84,14 @@ def e4m3_decode(bits):
     return np.where((b & 0x7F) == 0x7F, np.nan, s * val)
 
 
+def _codes_for_scales(blocks, g, s):
+    """e2m1 codes of fp32 blocks [..., nb, 16] under scales s [..., nb]
+    (E4M3 values) and global scale g: codes of fl(x / fl(s g))."""
+    d = (s.astype(_F32) * _F32(g)).astype(_F32)          # element divisor, fp32
+    q = (blocks / d[..., None]).astype(_F32)             # fp32 division, nearest-even
+    return e2m1_encode(q.astype(np.float64))
+
+
 def encode_with_global_scale(x, g):
     """Block scales and codes of x [..., K] (K % 16 == 0) given the tensor's
     global scale g (float32).  Returns (packed uint8 [..., K/2], block scale
@@ -91,12 +116,64 @@ def encode_with_global_scale(x, g):
         ratio = np.where(ratio == 0, _F32(1.0), ratio)
         ratio = np.clip(ratio, _F32(NVFP4_SCALE_MIN), _F32(E4M3_MAX))
         s = e4m3_round(ratio.astype(np.float64))
-        d = (s.astype(_F32) * g).astype(_F32)            # element divisor, fp32
-        q = (blocks / d[..., None]).astype(_F32)         # fp32 division, nearest-even
-        codes = e2m1_encode(q.astype(np.float64))
+        codes = _codes_for_scales(blocks, g, s)
     codes = codes.reshape(lead + (K,))
     packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
     return packed, e4m3_bits(s)
+
+
+def block_sq_errors(blocks, g, s):
+    """fp32 squared error of each block [..., 16] quantized with scale s [...]
+    (E4M3 values) and global scale g, in the reading's order.  Returns
+    (errors float32 [...], divisor d float32 [...])."""
+    d = (s.astype(_F32) * _F32(g)).astype(_F32)
+    codes = _codes_for_scales(blocks, g, s)
+    xhat = (E2M1_TABLE[codes.astype(np.int64)].astype(_F32) * d[..., None]).astype(_F32)
+    e = (blocks - xhat).astype(_F32)
+    sq = (e * e).astype(_F32)
+    acc = np.zeros(sq.shape[:-1], _F32)
+    with np.errstate(over="ignore"):
+        for i in range(sq.shape[-1]):
+            acc = (acc + sq[..., i]).astype(_F32)
+    return acc, d
+
+
+def mse_block_scales(x, g):
+    """The MSE rule's block scale codes (E4M3 bits, uint8 [..., K/16]) of x
+    [..., K] under global scale g (float32, nonzero)."""
+    x = np.asarray(x, dtype=np.float64)
+    K = x.shape[-1]
+    blocks = x.astype(_F32).reshape(x.shape[:-1] + (K // NVFP4_BLOCK, NVFP4_BLOCK))
+    best = np.zeros(blocks.shape[:-1], np.uint8)
+    best_err = np.zeros(best.shape, _F32)
+    for code in range(1, 0x7F):
+        s = np.full(best.shape, e4m3_decode(np.uint8(code)))
+        err, d = block_sq_errors(blocks, g, s)
+        take = (d != 0) & ((best == 0) | (err < best_err))
+        best = np.where(take, np.uint8(code), best)
+        best_err = np.where(take, err, best_err)
+    return best
+
+
+def quantize_nvfp4_mse(x):
+    """Two-level NVFP4 with MSE-searched block scales: x [..., K] (K % 16 ==
+    0) -> (packed uint8 [..., K/2], block scale bits uint8 [..., K/16], g
+    float32); dequantized by ``dequantize_nvfp4``."""
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("quantize_nvfp4_mse: non-finite input")
+    K = x.shape[-1]
+    if K % NVFP4_BLOCK != 0:
+        raise ValueError("quantize_nvfp4_mse: K must be divisible by 16")
+    g = global_scale(x)
+    if g == 0:
+        packed, scales = encode_with_global_scale(x, g)
+        return packed, scales, g
+    scales = mse_block_scales(x, g)
+    blocks = x.astype(_F32).reshape(x.shape[:-1] + (K // NVFP4_BLOCK, NVFP4_BLOCK))
+    codes = _codes_for_scales(blocks, g, e4m3_decode(scales)).reshape(x.shape)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return packed, scales, g
 
 
 def quantize_nvfp4(x):
@@ -132,4 +209,5 @@ def dequantize_nvfp4(packed, scale_bits, g, dtype):
 
 
 __all__ = ["NVFP4_BLOCK", "global_scale", "e4m3_bits", "e4m3_decode", "encode_with_global_scale",
-           "quantize_nvfp4", "dequantize_nvfp4_values", "dequantize_nvfp4"]
+           "quantize_nvfp4", "dequantize_nvfp4_values", "dequantize_nvfp4", "block_sq_errors",
+           "mse_block_scales", "quantize_nvfp4_mse"]

@@ -145,3 +145,102 @@ def test_nibble_order_and_shapes():
     assert packed[0, 0] == (7 | (9 << 4))
     with pytest.raises(ValueError):
         oracle.quantize_nvfp4(np.zeros((1, 24)))
+
+
+# ---- MSE block-scale rule ("Where the scales come from", NVFP4's own rules)
+
+E4M3_POS = oracle.e4m3_decode(np.arange(1, 0x7F, dtype=np.uint8))     # the 126 candidates
+
+
+def _exact_errors(block, g):
+    """Squared error (fp64) of one 16-block under each of the 126 candidates,
+    rounding x / d to the nearest e2m1 value (ties to the even code) in fp64:
+    an implementation independent of the oracle's fp32 steps."""
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    out = []
+    for s in E4M3_POS:
+        d = float(np.float32(np.float32(s) * np.float32(g)))
+        q = np.abs(block) / d
+        dist = np.abs(q[:, None] - grid[None, :])
+        best = dist.min(axis=1, keepdims=True)
+        cand = np.where(dist == best, np.arange(8)[None, :], 99)
+        even = np.where(cand % 2 == 0, cand, 99).min(axis=1)      # ties: the even code
+        idx = np.where(np.sum(dist == best, axis=1) > 1, even, cand.min(axis=1))
+        xhat = np.sign(block) * grid[idx] * d
+        out.append(float(np.sum((block - xhat) ** 2)))
+    return np.array(out)
+
+
+def test_mse_scale_is_the_least_error_candidate_by_brute_force():
+    x = rand_tensor(21, (4, 256), outliers=0.01)
+    packed, sb, g = oracle.quantize_nvfp4_mse(x)
+    blocks = x.reshape(4, 16, 16)
+    for r in range(4):
+        for b in range(16):
+            errs = _exact_errors(blocks[r, b], g)
+            chosen = errs[int(sb[r, b]) - 1]
+            assert chosen <= errs.min() * (1 + 1e-5) + 1e-300, (r, b, int(sb[r, b]), int(np.argmin(errs)) + 1)
+
+
+def test_mse_never_worse_than_the_max_rule():
+    """The max rule's scale is one of the 126 candidates, so the chosen
+    block's fp32 error is at most the max rule's, block by block; the sweep
+    also changes most blocks' scales and lowers the total error."""
+    x = rand_tensor(22, (32, 512), outliers=0.005)
+    p_m, s_m, g = oracle.quantize_nvfp4_mse(x)
+    p_x, s_x, g_x = oracle.quantize_nvfp4(x)
+    assert g == g_x
+    blocks = x.astype(np.float32).reshape(32, 32, 16)
+    e_m, _ = oracle.nvfp4_block_sq_errors(blocks, g, oracle.e4m3_decode(s_m))
+    e_x, _ = oracle.nvfp4_block_sq_errors(blocks, g, oracle.e4m3_decode(s_x))
+    assert np.all(e_m <= e_x)
+    nz = e_x > 0
+    assert (s_m != s_x).mean() > 0.3 and e_m.sum() < e_x.sum() and np.median(e_m[nz] / e_x[nz]) < 0.9
+    # the stored codes are the two-level encoding under the chosen scales
+    v = oracle.dequantize_nvfp4_values(p_m, s_m, g)
+    assert np.allclose(((v - x) ** 2).reshape(32, 32, 16).sum(-1), e_m, rtol=1e-5, atol=0)
+
+
+def test_mse_exact_blocks_come_back_exactly_with_the_first_exact_scale():
+    """Blocks of e2m1 grid values times an E4M3 value s and g = 2^t are
+    quantized without error; the scale kept is the smallest code that is
+    exact (a smaller scale that also represents the block wins)."""
+    g0 = np.random.default_rng(23)
+    t = -4
+    rows = []
+    rows.append(np.concatenate([[6.0 * 448.0], np.zeros(15)]) * 2.0 ** t)       # sets g = 2^t
+    for code in (0x01, 0x05, 0x21, 0x38, 0x4B, 0x7E):
+        s = float(oracle.e4m3_decode(np.uint8(code)))
+        vals = GRID[g0.integers(0, 8, 16)] * np.where(g0.random(16) < 0.5, -1.0, 1.0)
+        rows.append(vals * s * 2.0 ** t)
+    x = np.stack(rows)
+    packed, sb, g = oracle.quantize_nvfp4_mse(x)
+    assert g == np.float32(2.0 ** t)
+    assert np.array_equal(oracle.dequantize_nvfp4_values(packed, sb, g), x)
+    for r in range(x.shape[0]):
+        errs = _exact_errors(x[r], g)
+        assert errs[int(sb[r, 0]) - 1] == 0 and np.all(errs[: int(sb[r, 0]) - 1] > 0)
+
+
+def test_mse_zero_block_zero_tensor_and_subnormal_scales():
+    x = rand_tensor(24, (2, 64))
+    x[0, 16:32] = 0.0
+    gx = np.float32(np.abs(x).max()) / np.float32(2688.0)
+    x[1, 0:16] *= 6.0 * float(gx) * 2.0 ** -8 / np.abs(x[1, 0:16]).max()   # block ratio 2^-8: an E4M3 subnormal scale
+    x = x.astype(np.float32).astype(np.float64)
+    packed, sb, g = oracle.quantize_nvfp4_mse(x)
+    assert sb[0, 1] == 0x01 and np.all(packed[0, 8:16] == 0)        # every candidate is exact: the first
+    assert sb[1, 0] < 0x08                                          # subnormal candidates are in the sweep
+    errs = _exact_errors(x[1, :16], g)
+    assert errs[int(sb[1, 0]) - 1] <= errs.min() * (1 + 1e-5)
+    packed, sb, g = oracle.quantize_nvfp4_mse(np.zeros((2, 32)))
+    assert g == 0 and np.all(sb == 0x38) and np.all(packed == 0)
+
+
+def test_mse_power_of_two_scaling_moves_only_the_global_scale():
+    x = rand_tensor(25, (6, 128), outliers=0.01)
+    p0, s0, g0 = oracle.quantize_nvfp4_mse(x)
+    for t in (-20, -3, 5, 30):
+        p1, s1, g1 = oracle.quantize_nvfp4_mse(x * 2.0 ** t)
+        assert g1 == np.float32(g0 * 2.0 ** t)
+        assert np.array_equal(s1, s0) and np.array_equal(p1, p0)
