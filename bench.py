@@ -14,8 +14,11 @@ workload, all inputs already resident in HBM:
   nvfp4/16, and the straight-through backward copy; the packed storage form
   of each (codes + scale bytes) and its dequantize-on-read;
 * bulk bf16 [65536, 7168]: quantize_mxfp4, dequantize_mxfp4, quantize_cache
-  nvfp4/16, fp8/128 and mxfp4/32; dequantization of a 2^30-parameter
-  mxfp4 weight [64, 4096, 4096] to bf16;
+  nvfp4/16, fp8/128 and mxfp4/32, two-level NVFP4 quantize and dequantize;
+  the NVFP4 MSE block-scale sweep of a bf16 weight [4096, 7168] (VALU-bound:
+  reported against the fp32 issue rate, 6 operations per element and
+  candidate); dequantization of a 2^30-parameter mxfp4 weight
+  [64, 4096, 4096] to bf16;
 * mxfp4 round trip of an fp32 [256, 1024] tensor (latency-bound).
 
 Legs whose working set fits in the 256 MB Infinity Cache rotate over enough
@@ -37,6 +40,8 @@ import time
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 MFMA_FP4_PEAK_TFLOPS = 10100.0   # MI355X dense fp4 (MXFP4) MFMA
+# fp32 VALU issue rate without packed (two-wide) fp32 or FMA pairing: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+ALU_FP32_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 METRIC = "quant/dequant GB/s (% HBM peak); MXFP4 grouped-GEMM TFLOP/s (% MFMA peak)"
 
 
@@ -51,8 +56,9 @@ def parse():
 
 
 class Leg:
-    def __init__(self, name, kernel, kind, work, fn, reps=1, peak=None):
+    def __init__(self, name, kernel, kind, work, fn, reps=1, peak=None, alu_ops=None):
         self.name, self.kernel, self.kind, self.work, self.fn, self.reps = name, kernel, kind, work, fn, reps
+        self.alu_ops = alu_ops   # algorithmic fp32 operations per call, for a VALU-bound leg
         # the roof this leg's rate is a fraction of (TFLOP/s or GB/s)
         self.peak = peak or (MFMA_BF16_PEAK_TFLOPS if kind == "flop" else HBM_PEAK_GBPS)
         self.ms = 0.0   # summed event time over the timed steps
@@ -249,6 +255,17 @@ def main():
         legs.append(Leg("bulk.dequantize_nvfp4", "k_dequantize_nvfp4<bf16>", "byte", nb * (0.5 + 1 / 16 + 2),
                         lambda i: check(L.dequantize_nvfp4(npk.data_ptr(), nsc.data_ptr(), ng.data_ptr(), br, bc,
                                                            bdq.data_ptr(), 1, sp), "dqnv")))
+        # MSE block-scale sweep of one bf16 weight [4096, 7168]: 126 candidate scales per block of 16,
+        # bound by VALU throughput (bytes: the amax read + the sweep read + outputs)
+        nvw = bf16(synth.nvfp4_weight(seed=0)["w"])
+        mr, mc = nvw.shape
+        mpk = torch.empty(mr, mc // 2, dtype=torch.uint8, device=dev)
+        msc = torch.empty(mr, mc // 16, dtype=torch.uint8, device=dev)
+        mg = torch.zeros(1, dtype=torch.float32, device=dev)
+        legs.append(Leg("bulk.quantize_nvfp4_mse", "k_nvfp4_amax+k_quantize_nvfp4_mse<bf16>", "byte",
+                        nvw.numel() * (2 * 2 + 0.5 + 1 / 16),
+                        lambda i: check(L.quantize_nvfp4_mse(nvw.data_ptr(), 1, mr, mc, mpk.data_ptr(), msc.data_ptr(),
+                                                             mg.data_ptr(), sp), "qmse"), alu_ops=6.0 * 126 * nvw.numel()))
         nw = 64 * 4096 * 4096
         legs.append(Leg("bulk.weight_dequant", "k_dequantize_mxfp4<bf16>", "byte", nw * (0.5 + 1 / 32 + 2),
                         lambda i: check(L.dequantize_mxfp4(wp.data_ptr(), ws.data_ptr(), 64 * 4096, 4096,
@@ -308,6 +325,9 @@ def main():
         else:
             rate = leg.work / (per_call_ms * 1e-3) / 1e9
             d.update({"GB": round(leg.work / 1e9, 4), "GB/s": round(rate, 1), "frac_hbm": round(rate / HBM_PEAK_GBPS, 4)})
+        if leg.alu_ops:
+            tops = leg.alu_ops / (per_call_ms * 1e-3) / 1e12
+            d.update({"bound": "alu", "Tops/s": round(tops, 2), "frac_alu": round(tops / ALU_FP32_PEAK_TOPS, 4)})
         out_legs.append(d)
 
     moe_legs = [l for l in legs if l.name.startswith("moe.")]
@@ -315,7 +335,7 @@ def main():
     moe_flop = sum(l.work for l in moe_legs)
     moe_ms = sum(l.ms for l in moe_legs) / K
     value = moe_flop / (moe_ms * 1e-3) / 1e12 if moe_ms > 0 else None
-    codec = [l for l in legs if l.kind == "byte" and not l.name.startswith(("roundtrip", "w4a4."))]
+    codec = [l for l in legs if l.kind == "byte" and not l.alu_ops and not l.name.startswith(("roundtrip", "w4a4."))]
     codec_bytes = sum(l.work * l.reps for l in codec)
     codec_ms = sum(l.ms for l in codec) / K
     hbm_gbps = codec_bytes / (codec_ms * 1e-3) / 1e9 if codec_ms > 0 else None
@@ -361,7 +381,7 @@ def main():
             "workload": "routed-expert layer share (32 experts, hidden 7168, intermediate 2048, 131072 routed rows, "
                         "fwd + grad_x) + 8-expert GEMM [4096x4096 -> 2048] + bf16 KV cache [4,8192,512] fake-quant "
                         "fp8/128, mxfp4/32, nvfp4/16 + STE + packed KV store/load + bulk bf16 [65536,7168] codecs (mxfp4, two-level nvfp4, "
-                        "cache fake-quant) + [64,4096,4096] weight dequant + W4A4 routed-expert forwards",
+                        "cache fake-quant) + NVFP4 MSE scale sweep of a bf16 [4096,7168] weight + [64,4096,4096] weight dequant + W4A4 routed-expert forwards",
             "value_is": "grouped-GEMM TFLOP/s of the routed-expert layer legs (event time)",
             "moe_rows": moe_rows,
         },

@@ -159,6 +159,23 @@ int quantize_nvfp4(const void* x, int xt, int64_t rows, int64_t k, uint8_t* pack
                    float* global_scale, void* stream);
 
 /*
+ * quantize_nvfp4_mse -- [MO] section "Where the scales come from" (NVFP4's
+ * own rules, the `mse` rule): two-level NVFP4 as quantize_nvfp4 (same g,
+ * layouts, zero-tensor rule, arguments and errors), except that each block's
+ * scale is searched: every positive finite E4M3 value (codes 0x01 .. 0x7E, in
+ * that order) is tried as s_b and the first with the least squared error is
+ * kept.  The error of a candidate is computed in fp32, each operation rounded
+ * nearest-even, no fused multiply-add: d = fl(s_b g), codes of fl(x / d),
+ * e_i = fl(x_i - fl(e2m1(code_i) d)), summed fl(e_i e_i) over i = 0 .. 15 in
+ * order; a candidate whose d underflows to 0 is skipped.  The codes stored
+ * are those of fl(x / d) under the chosen scale, so dequantize_nvfp4 reads
+ * the result.  One thread per block of 16 (126 candidates each): bound by
+ * VALU throughput, not HBM.  Any alignment of x.
+ */
+int quantize_nvfp4_mse(const void* x, int xt, int64_t rows, int64_t k, uint8_t* packed, uint8_t* block_scales,
+                       float* global_scale, void* stream);
+
+/*
  * dequantize_nvfp4 -- the inverse of quantize_nvfp4 ([MO], same section):
  * out[i] = fl(e2m1(code_i) * fl(E4M3(s_b) * g)), rounded nearest-even to ot
  * (code 8 decodes to +0.0; an E4M3 NaN scale gives NaN).  global_scale is a

@@ -24,6 +24,7 @@ from .ops import (
     dequantize_cache_packed,
     quantize_mxfp4,
     quantize_nvfp4,
+    quantize_nvfp4_mse,
 )
 
 __all__ = [
@@ -33,4 +34,5 @@ __all__ = [
     "mxfp4_grouped_mm_fwd_w4a4", "mxfp4_grouped_mm_fwd_w4a4_quantized",
     "quantize_cache", "quantize_cache_bwd", "quantize_cache_forward", "quantize_mxfp4",
     "quantize_nvfp4", "dequantize_nvfp4", "quantize_cache_packed", "dequantize_cache_packed",
+    "quantize_nvfp4_mse",
 ]

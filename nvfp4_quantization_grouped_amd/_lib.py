@@ -17,7 +17,7 @@ MXQ_FMT_FP8, MXQ_FMT_MXFP4, MXQ_FMT_NVFP4 = 0, 1, 2
 
 EXPORTS = (
     "quantize_mxfp4", "dequantize_mxfp4", "quantize_cache", "quantize_cache_bwd", "quantize_nvfp4", "dequantize_nvfp4",
-    "quantize_cache_packed", "dequantize_cache_packed",
+    "quantize_cache_packed", "dequantize_cache_packed", "quantize_nvfp4_mse",
     "mxfp4_grouped_mm_fwd", "mxfp4_grouped_mm_bwd_x", "mxfp4_grouped_mm_fwd_w4a4", "mxq_status_string",
 )
 
@@ -31,6 +31,7 @@ _SIGS = {
     "quantize_cache_bwd": ([_vp, _vp, _int, _i64, _vp], _int),
     "quantize_nvfp4": ([_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp], _int),
     "dequantize_nvfp4": ([_vp, _vp, _vp, _i64, _i64, _vp, _int, _vp], _int),
+    "quantize_nvfp4_mse": ([_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp], _int),
     "quantize_cache_packed": ([_vp, _int, _i64, _i64, _int, _i32, _vp, _vp, _vp], _int),
     "dequantize_cache_packed": ([_vp, _vp, _i64, _i64, _int, _i32, _vp, _int, _vp], _int),
     "mxfp4_grouped_mm_fwd": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp], _int),

@@ -108,8 +108,10 @@ int dequantize_cache_packed(const uint8_t* codes, const uint8_t* scales, int64_t
                                                       (hipStream_t)stream));
 }
 
-int quantize_nvfp4(const void* x, int xt, int64_t rows, int64_t k, uint8_t* packed, uint8_t* block_scales,
-                   float* global_scale, void* stream) {
+// Checks shared by the two NVFP4 quantizers; MXQ_OK with *launch = false means nothing to do.
+static int nvfp4_quantize_check(const void* x, int xt, int64_t rows, int64_t k, const uint8_t* packed,
+                                const uint8_t* block_scales, const float* global_scale, bool* launch) {
+  *launch = false;
   if (rows < 0 || k < 0 || k % 16 != 0) return MXQ_ERR_SHAPE;
   if (!dtype_ok(xt)) return MXQ_ERR_DTYPE;
   if (rows == 0 || k == 0) return MXQ_OK;
@@ -120,7 +122,25 @@ int quantize_nvfp4(const void* x, int xt, int64_t rows, int64_t k, uint8_t* pack
       overlap(packed, n / 2, block_scales, n / 16) || overlap(packed, n / 2, global_scale, 4) ||
       overlap(block_scales, n / 16, global_scale, 4))
     return MXQ_ERR_ALIAS;
+  *launch = true;
+  return MXQ_OK;
+}
+
+int quantize_nvfp4(const void* x, int xt, int64_t rows, int64_t k, uint8_t* packed, uint8_t* block_scales,
+                   float* global_scale, void* stream) {
+  bool launch = false;
+  const int st = nvfp4_quantize_check(x, xt, rows, k, packed, block_scales, global_scale, &launch);
+  if (st != MXQ_OK || !launch) return st;
   return from_hip(mxq::launch_quantize_nvfp4(x, xt, rows, k, packed, block_scales, global_scale, (hipStream_t)stream));
+}
+
+int quantize_nvfp4_mse(const void* x, int xt, int64_t rows, int64_t k, uint8_t* packed, uint8_t* block_scales,
+                       float* global_scale, void* stream) {
+  bool launch = false;
+  const int st = nvfp4_quantize_check(x, xt, rows, k, packed, block_scales, global_scale, &launch);
+  if (st != MXQ_OK || !launch) return st;
+  return from_hip(
+      mxq::launch_quantize_nvfp4_mse(x, xt, rows, k, packed, block_scales, global_scale, (hipStream_t)stream));
 }
 
 int dequantize_nvfp4(const uint8_t* packed, const uint8_t* block_scales, const float* global_scale, int64_t rows,

@@ -688,6 +688,99 @@ __global__ void __launch_bounds__(kThreads) k_dequantize_nvfp4_general(const uin
   }
 }
 
+// ------------------------------------------------------- NVFP4 MSE scale sweep
+// The MSE block-scale rule: each block of 16 tries the 126 positive finite
+// E4M3 values (codes 0x01 .. 0x7E, in order) as its scale and keeps the first
+// with the least fp32 squared error sum((x - fl(e2m1(fl(x / d)) d))^2), d =
+// fl(s g), products and sums rounded one by one, elements in order.  One lane
+// per block; d and its reciprocal are wave-uniform.  The error needs only the
+// code magnitudes, which the reciprocal bracket of nvfp4_encode_chunk gives
+// (x times rcp(d)(1 -+ 2^-20): where the two codes agree, no midpoint lies
+// between them); lanes whose bracket straddles a midpoint take divisions.
+// The stored codes are then encoded as the max rule's are.
+
+// Squared error of 8 elements (v) whose codes are the dword c, under d; adds
+// into err in element order.  Both products are kept opaque so that no
+// multiply-add fusion changes the rounding.
+__device__ __forceinline__ float sweep_err8(const float* v, uint32_t c, float d, float err) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    f32x2_t e2;
+    switch (p) {
+      case 0: e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0); break;
+      case 1: e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1); break;
+      case 2: e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2); break;
+      default: e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3); break;
+    }
+    const float e0 = v[2 * p] - mul_f32(e2.x, d), e1 = v[2 * p + 1] - mul_f32(e2.y, d);
+    err = err + mul_f32(e0, e0);
+    err = err + mul_f32(e1, e1);
+  }
+  return err;
+}
+
+// Codes of 8 values under reciprocal bracket factors rd = r(1 - 2^-20), ru =
+// r(1 + 2^-20); exact (IEEE division by d) where the bracket does not decide.
+__device__ __forceinline__ uint32_t sweep_codes8(const float* v, float rd, float ru, float d, bool force_exact) {
+  uint32_t lo = 0, hi = 0;
+  lo = enc_fp4_f2<0>(lo, v[0] * rd, v[1] * rd, 1.0f);
+  hi = enc_fp4_f2<0>(hi, v[0] * ru, v[1] * ru, 1.0f);
+  lo = enc_fp4_f2<1>(lo, v[2] * rd, v[3] * rd, 1.0f);
+  hi = enc_fp4_f2<1>(hi, v[2] * ru, v[3] * ru, 1.0f);
+  lo = enc_fp4_f2<2>(lo, v[4] * rd, v[5] * rd, 1.0f);
+  hi = enc_fp4_f2<2>(hi, v[4] * ru, v[5] * ru, 1.0f);
+  lo = enc_fp4_f2<3>(lo, v[6] * rd, v[7] * rd, 1.0f);
+  hi = enc_fp4_f2<3>(hi, v[6] * ru, v[7] * ru, 1.0f);
+  if (lo == hi && !force_exact) return lo;
+  uint32_t c = 0;
+  c = enc_fp4_f2<0>(c, v[0] / d, v[1] / d, 1.0f);
+  c = enc_fp4_f2<1>(c, v[2] / d, v[3] / d, 1.0f);
+  c = enc_fp4_f2<2>(c, v[4] / d, v[5] / d, 1.0f);
+  c = enc_fp4_f2<3>(c, v[6] / d, v[7] / d, 1.0f);
+  return c;
+}
+
+template <int DT>
+__global__ void __launch_bounds__(kThreads) k_quantize_nvfp4_mse(const uint8_t* __restrict__ x,
+                                                               uint8_t* __restrict__ packed,
+                                                               uint8_t* __restrict__ scales, int64_t nblocks,
+                                                               const uint32_t* __restrict__ slot) {
+  const float g = as_f32(*slot) / kNvfp4Den;
+  for (int64_t b = (int64_t)blockIdx.x * kThreads + threadIdx.x; b < nblocks; b += (int64_t)gridDim.x * kThreads) {
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = load_elem<DT>(x, b * 16 + i) + 0.0f;
+    uint32_t best = 0x38, w0 = 0, w1 = 0;
+    if (g != 0.0f) {
+      best = 0;
+      float best_err = 0.0f;
+      for (uint32_t code = 1; code < 0x7F; ++code) {
+        const float d = dec_fp8_f2<false>(code, 1.0f).x * g;
+        if (d == 0.0f) continue;                     // the divisor underflowed: not a candidate
+        const float r = __builtin_amdgcn_rcpf(d);
+        const bool force_exact = !(r <= 0x1p126f);
+        const float rd = r * (1.0f - 0x1p-20f), ru = r * (1.0f + 0x1p-20f);
+        const uint32_t c0 = sweep_codes8(v, rd, ru, d, force_exact);
+        const uint32_t c1 = sweep_codes8(v + 8, rd, ru, d, force_exact);
+        const float err = sweep_err8(v + 8, c1, d, sweep_err8(v, c0, d, 0.0f));
+        if (best == 0 || err < best_err) { best = code; best_err = err; }
+      }
+      const float d = dec_fp8_f2<false>(best, 1.0f).x * g;
+      Chunk<DT_F32> h0, h1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { h0.w[i] = as_u32(v[i]); h1.w[i] = as_u32(v[8 + i]); }
+      w0 = nvfp4_encode_chunk<DT_F32>(h0, d);
+      w1 = nvfp4_encode_chunk<DT_F32>(h1, d);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      packed[b * 8 + j] = (uint8_t)(w0 >> (8 * j));
+      packed[b * 8 + 4 + j] = (uint8_t)(w1 >> (8 * j));
+    }
+    scales[b] = (uint8_t)best;
+  }
+}
+
 // ------------------------------------------------- packed KV-cache storage
 // The codes and group scales quantize_cache rounds through, stored: e2m1
 // nibbles (even channel low, sign bit for x < 0) or E4M3 bytes, and one scale
@@ -1117,6 +1210,45 @@ hipError_t launch_quantize_nvfp4(const void* x, int dt, int64_t rows, int64_t k,
     case DT_F32: return launch_quantize_nvfp4_t<DT_F32>(x, rows, k, packed, scales, global_scale, st);
     case DT_BF16: return launch_quantize_nvfp4_t<DT_BF16>(x, rows, k, packed, scales, global_scale, st);
     default: return launch_quantize_nvfp4_t<DT_F16>(x, rows, k, packed, scales, global_scale, st);
+  }
+}
+
+template <int DT>
+static hipError_t launch_quantize_nvfp4_mse_t(const void* x, int64_t rows, int64_t k, uint8_t* packed,
+                                              uint8_t* scales, float* gscale, hipStream_t st) {
+  const int64_t n = rows * k;
+  uint32_t* slot = reinterpret_cast<uint32_t*>(gscale);
+  hipLaunchKernelGGL(k_nvfp4_amax_init, dim3(1), dim3(1), 0, st, slot);
+  if (aligned(x, 16)) {
+    const int64_t nchunks = n / 8, bytes = n * (DT == DT_F32 ? 4 : 2);
+    if (bytes >= kBigStreamBytes)
+      hipLaunchKernelGGL((k_nvfp4_amax<DT, StreamBig>),
+                         dim3(std::min(grid_for(nchunks, kThreads * StreamBig::kUnroll), kAmaxGridCap)), dim3(kThreads),
+                         0, st, (const uint8_t*)x, nchunks, slot);
+    else if (bytes >= kTinyStreamBytes)
+      hipLaunchKernelGGL((k_nvfp4_amax<DT, StreamSmall>),
+                         dim3(std::min(grid_for(nchunks, kThreads * StreamSmall::kUnroll), kAmaxGridCap)),
+                         dim3(kThreads), 0, st, (const uint8_t*)x, nchunks, slot);
+    else
+      hipLaunchKernelGGL((k_nvfp4_amax<DT, StreamTiny>),
+                         dim3(std::min(grid_for(nchunks, kThreads * StreamTiny::kUnroll), kAmaxGridCap)),
+                         dim3(kThreads), 0, st, (const uint8_t*)x, nchunks, slot);
+  } else {
+    hipLaunchKernelGGL(k_nvfp4_amax_general<DT>, dim3(std::min(grid_for(n, kThreads * 16), kAmaxGridCap)),
+                       dim3(kThreads), 0, st, (const uint8_t*)x, n, slot);
+  }
+  hipLaunchKernelGGL(k_quantize_nvfp4_mse<DT>, dim3(grid_for(n / 16, kThreads)), dim3(kThreads), 0, st,
+                     (const uint8_t*)x, packed, scales, n / 16, (const uint32_t*)slot);
+  hipLaunchKernelGGL(k_nvfp4_finalize, dim3(1), dim3(1), 0, st, slot);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_nvfp4_mse(const void* x, int dt, int64_t rows, int64_t k, uint8_t* packed,
+                                     uint8_t* scales, float* global_scale, hipStream_t st) {
+  switch (dt) {
+    case DT_F32: return launch_quantize_nvfp4_mse_t<DT_F32>(x, rows, k, packed, scales, global_scale, st);
+    case DT_BF16: return launch_quantize_nvfp4_mse_t<DT_BF16>(x, rows, k, packed, scales, global_scale, st);
+    default: return launch_quantize_nvfp4_mse_t<DT_F16>(x, rows, k, packed, scales, global_scale, st);
   }
 }
 

@@ -17,6 +17,9 @@ hipError_t launch_quantize_cache(const void* x, void* out, int dt, int64_t rows,
 // Two-level NVFP4: packed e2m1 [n/2], E4M3 block-16 scales [n/16], FP32 global scale (1 float, device).
 hipError_t launch_quantize_nvfp4(const void* x, int dt, int64_t rows, int64_t k, uint8_t* packed, uint8_t* scales,
                                  float* global_scale, hipStream_t st);
+// Same outputs with the block scales chosen by the MSE sweep over the 126 positive finite E4M3 values.
+hipError_t launch_quantize_nvfp4_mse(const void* x, int dt, int64_t rows, int64_t k, uint8_t* packed, uint8_t* scales,
+                                     float* global_scale, hipStream_t st);
 hipError_t launch_dequantize_nvfp4(const uint8_t* packed, const uint8_t* scales, const float* global_scale,
                                    int64_t rows, int64_t k, void* out, int dt, hipStream_t st);
 // Packed cache storage: codes [n] (fp8) or [n/2] (e2m1), one scale byte per group; whole groups only.

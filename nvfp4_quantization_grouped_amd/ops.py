@@ -94,6 +94,25 @@ def dequantize_mxfp4(packed, scales, dtype):
 _E4M3 = getattr(torch, "float8_e4m3fn", None)
 
 
+def _quantize_nvfp4(x, name):
+    _need_cuda(x)
+    if x.dtype not in _DT:
+        raise TypeError(f"{name}: unsupported dtype {x.dtype}")
+    K = x.shape[-1] if x.dim() else 0
+    if K % 16:
+        raise ValueError(f"{name}: K must be divisible by 16")
+    x = x.contiguous()
+    rows = x.numel() // K if K else 0
+    packed = torch.empty(*x.shape[:-1], K // 2, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(*x.shape[:-1], K // 16, dtype=torch.uint8, device=x.device)
+    g = torch.zeros((), dtype=torch.float32, device=x.device)
+    with torch.cuda.device(x.device):
+        st = getattr(_lib.lib(), name)(_ptr(x), _DT[x.dtype], rows, K, _ptr(packed), _ptr(scales), g.data_ptr(),
+                                       _stream(x.device))
+    _lib.check(st, name)
+    return packed, (scales.view(_E4M3) if _E4M3 is not None else scales), g
+
+
 def quantize_nvfp4(x):
     """Two-level NVFP4 ("NVIDIA Model Optimizer: from mtq.quantize to a
     4.95-bit DeepSeek-R1", section "NVFP4 in the code: two scales and a
@@ -101,22 +120,14 @@ def quantize_nvfp4(x):
     float8_e4m3fn block scales [..., K/16], float32 global scale g [] on the
     device), the four-tensor checkpoint layout's weight, weight_scale and
     weight_scale_2."""
-    _need_cuda(x)
-    if x.dtype not in _DT:
-        raise TypeError(f"quantize_nvfp4: unsupported dtype {x.dtype}")
-    K = x.shape[-1] if x.dim() else 0
-    if K % 16:
-        raise ValueError("quantize_nvfp4: K must be divisible by 16")
-    x = x.contiguous()
-    rows = x.numel() // K if K else 0
-    packed = torch.empty(*x.shape[:-1], K // 2, dtype=torch.uint8, device=x.device)
-    scales = torch.empty(*x.shape[:-1], K // 16, dtype=torch.uint8, device=x.device)
-    g = torch.zeros((), dtype=torch.float32, device=x.device)
-    with torch.cuda.device(x.device):
-        st = _lib.lib().quantize_nvfp4(_ptr(x), _DT[x.dtype], rows, K, _ptr(packed), _ptr(scales), g.data_ptr(),
-                                       _stream(x.device))
-    _lib.check(st, "quantize_nvfp4")
-    return packed, (scales.view(_E4M3) if _E4M3 is not None else scales), g
+    return _quantize_nvfp4(x, "quantize_nvfp4")
+
+
+def quantize_nvfp4_mse(x):
+    """Two-level NVFP4 with each block scale searched over the 126 positive
+    finite E4M3 values for the least squared error (same page, section "Where
+    the scales come from"); outputs as ``quantize_nvfp4``."""
+    return _quantize_nvfp4(x, "quantize_nvfp4_mse")
 
 
 def dequantize_nvfp4(packed, block_scales, global_scale, dtype):

@@ -28,6 +28,9 @@ Workloads (the shapes of the KV caches and MoE expert weights on the pages):
 * ``bulk_stream``     bf16 [65536, 7168] normal(0,1) with per-row scale 2^k, k
   uniform integer in [-4, 4]; a 2^30-parameter packed weight [64, 4096, 2048]
   with scale bytes [64, 4096, 128] in {117..123}.
+* ``nvfp4_weight``    bf16 [4096, 7168] (one expert's fused gate/up weight),
+  normal(0, 0.02 * 2^k) with k in {-1, 0, 1} per row, 0.1% of the entries
+  multiplied by uniform(4, 16) (NVFP4 MSE scale sweep).
 """
 
 import numpy as np
@@ -165,3 +168,19 @@ def bulk_stream(seed=0, rows=65536, cols=7168, with_weights=True):
     if with_weights:
         out["w_packed"], out["w_scales"] = packed_weights(g_b, g_s, 64, 4096, 4096)
     return out
+
+
+def nvfp4_weight(seed=0, rows=4096, cols=7168, std=0.02, outlier_frac=0.001):
+    """bf16 weight [rows, cols] (one routed expert's fused gate/up projection,
+    2 x 2048 outputs over hidden 7168): normal(0, std * 2^k) with k in
+    {-1, 0, 1} per output row, and outlier_frac of the entries multiplied by
+    U(4, 16)."""
+    g_x, g_k, g_pick, g_mag = streams(seed, 4)
+    k = g_k.integers(-1, 2, size=rows)
+    v = g_x.standard_normal((rows, cols), dtype=np.float32)
+    v *= (np.float32(std) * np.ldexp(np.float32(1.0), k)[:, None]).astype(np.float32)
+    n_out = int(outlier_frac * v.size)
+    idx = g_pick.choice(v.size, size=n_out, replace=False)
+    v.reshape(-1)[idx] *= g_mag.uniform(4.0, 16.0, size=n_out).astype(np.float32)
+    return {"w": f32_to_bf16_bits(v), "row_pow": k}
+

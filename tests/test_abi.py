@@ -176,3 +176,15 @@ def test_cache_packed_validation(L):
     assert d(FAKE, None, 4, 64, 1, 32, FAKE * 3, 1, None) == -1
     assert d(FAKE, FAKE * 2, 4, 64, 1, 32, FAKE - 100, 1, None) == -7      # out over the codes
     assert d(FAKE, FAKE * 2, 0, 64, 1, 32, FAKE * 3, 1, None) == 0
+
+
+def test_nvfp4_mse_validation(L):
+    q = L.quantize_nvfp4_mse
+    # (x, dtype, rows, k, packed, block_scales, global_scale, stream): quantize_nvfp4's checks
+    assert q(FAKE, 1, 4, 24, FAKE * 2, FAKE * 3, FAKE * 4, None) == -2
+    assert q(FAKE, 3, 4, 32, FAKE * 2, FAKE * 3, FAKE * 4, None) == -3
+    assert q(FAKE, 1, 4, 32, None, FAKE * 3, FAKE * 4, None) == -1
+    assert q(FAKE, 1, 4, 32, FAKE * 2, FAKE * 3, FAKE * 4 + 1, None) == -6
+    assert q(FAKE, 1, 4, 32, FAKE * 2, FAKE * 2 + 8, FAKE * 4, None) == -7   # scales inside packed
+    assert q(FAKE, 1, 4, 0, FAKE * 2, FAKE * 3, FAKE * 4, None) == 0
+
