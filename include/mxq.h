@@ -165,9 +165,10 @@ int quantize_nvfp4(const void* x, int xt, int64_t rows, int64_t k, uint8_t* pack
  * scale is searched: every positive finite E4M3 value (codes 0x01 .. 0x7E, in
  * that order) is tried as s_b and the first with the least squared error is
  * kept.  The error of a candidate is computed in fp32, each operation rounded
- * nearest-even, no fused multiply-add: d = fl(s_b g), codes of fl(x / d),
- * e_i = fl(x_i - fl(e2m1(code_i) d)), summed fl(e_i e_i) over i = 0 .. 15 in
- * order; a candidate whose d underflows to 0 is skipped.  The codes stored
+ * nearest-even: d = fl(s_b g), codes of fl(x / d), e_i = x_i -
+ * e2m1(code_i) d rounded once (a fused multiply-add), then fl(e_i e_i)
+ * summed over i = 0 .. 15 in order, each sum rounded; a candidate whose d
+ * underflows to 0 is skipped.  The codes stored
  * are those of fl(x / d) under the chosen scale, so dequantize_nvfp4 reads
  * the result.  One thread per block of 16 (126 candidates each): bound by
  * VALU throughput, not HBM.  Any alignment of x.

@@ -691,8 +691,9 @@ __global__ void __launch_bounds__(kThreads) k_dequantize_nvfp4_general(const uin
 // ------------------------------------------------------- NVFP4 MSE scale sweep
 // The MSE block-scale rule: each block of 16 tries the 126 positive finite
 // E4M3 values (codes 0x01 .. 0x7E, in order) as its scale and keeps the first
-// with the least fp32 squared error sum((x - fl(e2m1(fl(x / d)) d))^2), d =
-// fl(s g), products and sums rounded one by one, elements in order.  One lane
+// with the least fp32 squared error sum(fl(e^2)), e = x - e2m1(fl(x / d)) d in
+// one fused multiply-add, d = fl(s g), squares and sums rounded one by one,
+// elements in order.  One lane
 // per block; d and its reciprocal are wave-uniform.  The error needs only the
 // code magnitudes, which the reciprocal bracket of nvfp4_encode_chunk gives
 // (x times rcp(d)(1 -+ 2^-20): where the two codes agree, no midpoint lies
@@ -700,8 +701,8 @@ __global__ void __launch_bounds__(kThreads) k_dequantize_nvfp4_general(const uin
 // The stored codes are then encoded as the max rule's are.
 
 // Squared error of 8 elements (v) whose codes are the dword c, under d; adds
-// into err in element order.  Both products are kept opaque so that no
-// multiply-add fusion changes the rounding.
+// into err in element order.  The residual is one fused multiply-add; the
+// square is kept opaque so that it is not fused into the sum.
 __device__ __forceinline__ float sweep_err8(const float* v, uint32_t c, float d, float err) {
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
@@ -712,7 +713,7 @@ __device__ __forceinline__ float sweep_err8(const float* v, uint32_t c, float d,
       case 2: e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2); break;
       default: e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3); break;
     }
-    const float e0 = v[2 * p] - mul_f32(e2.x, d), e1 = v[2 * p + 1] - mul_f32(e2.y, d);
+    const float e0 = __builtin_fmaf(-e2.x, d, v[2 * p]), e1 = __builtin_fmaf(-e2.y, d, v[2 * p + 1]);
     err = err + mul_f32(e0, e0);
     err = err + mul_f32(e1, e1);
   }

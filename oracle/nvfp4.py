@@ -35,9 +35,12 @@ least squared error against x.  Readings:
 * g is the max rule's global scale; for each candidate the codes and the
   dequantized values are the two-level ones above (d = fl(s g), codes of
   fl(x / d), x_hat = fl(e2m1 * d)).
-* The error is computed in fp32 in a fixed order: e_i = fl(x_i - x_hat_i),
-  fl(e_i * e_i), summed i = 0 .. 15 left to right, each sum rounded (no
-  fused multiply-add).  The candidate chosen is the first, in increasing
+* The error is computed in fp32 in a fixed order: e_i = x_i - e2m1_i * d
+  rounded once (a fused multiply-add; x_hat_i itself is not rounded first),
+  fl(e_i * e_i), summed i = 0 .. 15 left to right, each sum rounded.  The
+  fused e_i is exact to emulate: e2m1_i * d has at most 26 significant bits
+  and x_i and e2m1_i * d are at most about 2^18 apart, so their difference is
+  exact in float64 and one cast rounds it as the fused operation does.  The candidate chosen is the first, in increasing
   code order, with an error strictly below every earlier one; candidates
   whose d underflows to 0 are skipped.  An all-zero block therefore gets
   code 0x01 (every candidate is exact), and g = 0 gives the max rule's
@@ -128,8 +131,8 @@ def block_sq_errors(blocks, g, s):
     (errors float32 [...], divisor d float32 [...])."""
     d = (s.astype(_F32) * _F32(g)).astype(_F32)
     codes = _codes_for_scales(blocks, g, s)
-    xhat = (E2M1_TABLE[codes.astype(np.int64)].astype(_F32) * d[..., None]).astype(_F32)
-    e = (blocks - xhat).astype(_F32)
+    vd = E2M1_TABLE[codes.astype(np.int64)] * d.astype(np.float64)[..., None]      # exact in float64
+    e = (blocks.astype(np.float64) - vd).astype(_F32)                               # one rounding (fused)
     sq = (e * e).astype(_F32)
     acc = np.zeros(sq.shape[:-1], _F32)
     with np.errstate(over="ignore"):

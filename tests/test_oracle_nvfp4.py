@@ -244,3 +244,23 @@ def test_mse_power_of_two_scaling_moves_only_the_global_scale():
         p1, s1, g1 = oracle.quantize_nvfp4_mse(x * 2.0 ** t)
         assert g1 == np.float32(g0 * 2.0 ** t)
         assert np.array_equal(s1, s0) and np.array_equal(p1, p0)
+
+
+def test_mse_fused_residual_is_exact_in_float64():
+    """The oracle forms the fused residual x - e2m1 * d in float64 and rounds
+    it once to fp32; that equals the fused multiply-add only if the float64
+    difference is exact.  Checked with exact rationals over every candidate
+    of blocks whose quotients saturate (small scales) or round to zero."""
+    from fractions import Fraction
+    x = rand_tensor(26, (2, 64), outliers=0.05)
+    g = oracle.nvfp4_global_scale(x)
+    blocks = x.astype(np.float32).reshape(2, 4, 16)
+    for code in range(1, 0x7F):
+        s = np.full((2, 4), oracle.e4m3_decode(np.uint8(code)))
+        d = (s.astype(np.float32) * np.float32(g)).astype(np.float32)
+        codes = oracle.nvfp4._codes_for_scales(blocks, g, s)
+        vd = oracle.E2M1_TABLE[codes.astype(np.int64)] * d.astype(np.float64)[..., None]
+        diff = blocks.astype(np.float64) - vd
+        for xi, vi, di, df in zip(blocks.reshape(-1), oracle.E2M1_TABLE[codes.astype(np.int64)].reshape(-1),
+                                  np.repeat(d.reshape(-1), 16), diff.reshape(-1)):
+            assert Fraction(float(xi)) - Fraction(float(vi)) * Fraction(float(di)) == Fraction(float(df))
