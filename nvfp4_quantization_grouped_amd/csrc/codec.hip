@@ -484,19 +484,52 @@ __device__ __forceinline__ uint32_t nvfp4_block_scale(float ab, float g, float& 
   return bits;
 }
 
+// The same block scale from the reciprocal of 6g.  Per kernel: rlo, rhi =
+// rcp(fl(6g)) (1 -+ 2^-20) and fast = 6g in [2^-125, 2^125] (a normal,
+// accurate reciprocal).  ab rlo and ab rhi are within ~2 ulp of the nudged
+// quotients, so they bracket fl(ab / fl(6g)); where both cast to the same
+// E4M3 byte and lie inside (2^-8, 400) -- clear of the zero rule and the
+// clamp -- that byte is the cast of the correctly rounded ratio.  Otherwise
+// the division decides.
+struct Nvfp4Ratio {
+  float rlo, rhi;
+  bool fast;
+};
+__device__ __forceinline__ Nvfp4Ratio nvfp4_ratio_setup(float g) {
+  const float sixg = 6.0f * g;
+  const float r = __builtin_amdgcn_rcpf(sixg);
+  return {r * (1.0f - 0x1p-20f), r * (1.0f + 0x1p-20f), sixg >= 0x1p-125f && sixg <= 0x1p125f};
+}
+__device__ __forceinline__ uint32_t nvfp4_block_scale_fast(float ab, float g, const Nvfp4Ratio& q, float& d) {
+  if (q.fast) {
+    const float lo = ab * q.rlo, hi = ab * q.rhi;
+    if (lo >= 0x1p-8f && hi <= 400.0f) {
+      const uint32_t pr = enc_fp8_f2<false>(0u, lo, hi, 1.0f);     // bytes 0, 1: casts of lo, hi
+      if (((pr ^ (pr >> 8)) & 0xFFu) == 0u) {
+        const uint32_t bits = pr & 0xFFu;
+        d = dec_fp8_f2<false>(bits, 1.0f).x * g;
+        return bits;
+      }
+    }
+  }
+  return nvfp4_block_scale(ab, g, d);
+}
+
 // Eight elements -> eight e2m1 codes of the correctly rounded x / d (a
 // code's sign bit is x < 0: -0.0 gives code 0).  Fast form: with r the
 // hardware reciprocal of d (within 1 ulp), x r is within ~2.5 ulp of x / d, so the codes of
 // x r nudged down and up by 2^-20 (8 ulp) bracket the code of fl(x / d);
 // where the two agree no e2m1 midpoint lies between them and that is the
-// code.  A code of magnitude 0 keeps the sign of fl(x / d), which is -0.0
-// (code 0) for a negative x with |x / d| <= 2^-150, a boundary the
-// reciprocal product cannot see; with d < 256 only nonzero fp32 subnormal
-// inputs are that small (bf16 and f16 values are not).  So chunks with an
-// element within reach of a midpoint (exact ties among them), with d >= 256
-// or a reciprocal past 2^126, or with a nonzero fp32 subnormal input take
-// IEEE divisions.  About half the VALU work of a division per element, and
-// this pass is bound by it.
+// code.  The nudges are folded into the reciprocal (x r(1 -+ 2^-20), ~2 ulp
+// from the nudged quotients), and each product is a fused multiply-add with
+// +0.0, which maps a -0.0 input to +0.0 (code 0) at no extra cost and keeps
+// every other product as is.  A code of magnitude 0 keeps the sign of
+// fl(x / d), which is -0.0 (code 0) for a negative x with |x / d| <= 2^-150,
+// a boundary the reciprocal product cannot see; with d < 256 only nonzero
+// fp32 subnormal inputs are that small (bf16 and f16 values are not).  So
+// chunks with an element within reach of a midpoint (exact ties among them),
+// with d >= 256 or a reciprocal past 2^126, or with a nonzero fp32 subnormal
+// input take IEEE divisions.
 template <int DT>
 __device__ __forceinline__ uint32_t nvfp4_encode_chunk(const Chunk<DT>& ch, float d) {
   float v[8];
@@ -510,22 +543,20 @@ __device__ __forceinline__ uint32_t nvfp4_encode_chunk(const Chunk<DT>& ch, floa
 #pragma unroll
     for (int i = 0; i < 4; ++i) { v[2 * i] = f16_lo(ch.w[i]); v[2 * i + 1] = f16_hi(ch.w[i]); }
   }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] += 0.0f;   // -0.0 -> +0.0
   const float r = __builtin_amdgcn_rcpf(d);
-  constexpr float kDown = 1.0f - 0x1p-20f, kUp = 1.0f + 0x1p-20f;
-  float q[8];
+  const float rd = r * (1.0f - 0x1p-20f), ru = r * (1.0f + 0x1p-20f);
+  float ql[8], qh[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = v[i] * r;
+  for (int i = 0; i < 8; ++i) { ql[i] = __builtin_fmaf(v[i], rd, 0.0f); qh[i] = __builtin_fmaf(v[i], ru, 0.0f); }
   uint32_t lo = 0, hi = 0;
-  lo = enc_fp4_f2<0>(lo, q[0] * kDown, q[1] * kDown, 1.0f);
-  hi = enc_fp4_f2<0>(hi, q[0] * kUp, q[1] * kUp, 1.0f);
-  lo = enc_fp4_f2<1>(lo, q[2] * kDown, q[3] * kDown, 1.0f);
-  hi = enc_fp4_f2<1>(hi, q[2] * kUp, q[3] * kUp, 1.0f);
-  lo = enc_fp4_f2<2>(lo, q[4] * kDown, q[5] * kDown, 1.0f);
-  hi = enc_fp4_f2<2>(hi, q[4] * kUp, q[5] * kUp, 1.0f);
-  lo = enc_fp4_f2<3>(lo, q[6] * kDown, q[7] * kDown, 1.0f);
-  hi = enc_fp4_f2<3>(hi, q[6] * kUp, q[7] * kUp, 1.0f);
+  lo = enc_fp4_f2<0>(lo, ql[0], ql[1], 1.0f);
+  hi = enc_fp4_f2<0>(hi, qh[0], qh[1], 1.0f);
+  lo = enc_fp4_f2<1>(lo, ql[2], ql[3], 1.0f);
+  hi = enc_fp4_f2<1>(hi, qh[2], qh[3], 1.0f);
+  lo = enc_fp4_f2<2>(lo, ql[4], ql[5], 1.0f);
+  hi = enc_fp4_f2<2>(hi, qh[4], qh[5], 1.0f);
+  lo = enc_fp4_f2<3>(lo, ql[6], ql[7], 1.0f);
+  hi = enc_fp4_f2<3>(hi, qh[6], qh[7], 1.0f);
   bool exact = !(r <= 0x1p126f) || !(d < 256.0f);
   if constexpr (DT == DT_F32) {
 #pragma unroll
@@ -546,6 +577,7 @@ __global__ void __launch_bounds__(kThreads) k_quantize_nvfp4(const uint8_t* __re
                                                            uint8_t* __restrict__ scales, int64_t nchunks,
                                                            const uint32_t* __restrict__ slot) {
   const float g = as_f32(*slot) / kNvfp4Den;
+  const Nvfp4Ratio rq = nvfp4_ratio_setup(g);
   const int64_t step = (int64_t)gridDim.x * kThreads * M::kUnroll;
   for (int64_t base = (int64_t)blockIdx.x * kThreads * M::kUnroll; base < nchunks; base += step) {
     Chunk<DT> ch[M::kUnroll];
@@ -565,7 +597,7 @@ __global__ void __launch_bounds__(kThreads) k_quantize_nvfp4(const uint8_t* __re
       uint32_t codes = 0u, sbits = 0x38u;                                  // g = 0: scale 1.0, codes 0
       if (g != 0.0f) {
         float d;
-        sbits = nvfp4_block_scale(as_f32(ab), g, d);
+        sbits = nvfp4_block_scale_fast(as_f32(ab), g, rq, d);
         codes = nvfp4_encode_chunk<DT>(ch[u], d);
       }
       if (c < nchunks) {
