@@ -221,6 +221,8 @@ def dequantize_cache_packed(codes, scales, format, block_size, dtype):
     if format not in _FMT:
         raise ValueError("dequantize_cache_packed: format must be 'fp8', 'mxfp4' or 'nvfp4'")
     c = codes.contiguous()
+    if _E4M3 is not None and scales.dtype == _E4M3:       # nvfp4 scale bytes viewed as E4M3
+        scales = scales.view(torch.uint8)
     s = _as_u8(scales).contiguous()
     if c.dtype != torch.uint8 or c.dim() == 0:
         raise TypeError("dequantize_cache_packed: codes must be a uint8 tensor")
