@@ -2,7 +2,8 @@
 
     python -m nvfp4_quantization_grouped_amd.build
 
-Compiles every csrc/*.hip file with hipcc for gfx950 and links them into
+Compiles every csrc/*.hip file (kernels) and csrc/*.cpp file (the host-side
+C ABI) with hipcc for gfx950 and links them into
 nvfp4_quantization_grouped_amd/libmxq.so.  hipcc cross-compiles, so this runs
 on a machine without a GPU.
 """
@@ -52,9 +53,9 @@ def _compile(src, extra):
 
 
 def build(verbose=True, extra_flags=()):
-    """Compile all csrc/*.hip and link libmxq.so; returns the library path."""
+    """Compile all csrc/*.hip and csrc/*.cpp and link libmxq.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
     tmp = LIB + ".tmp"
