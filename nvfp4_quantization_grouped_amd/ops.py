@@ -221,9 +221,22 @@ def dequantize_cache_packed(codes, scales, format, block_size, dtype):
     if format not in _FMT:
         raise ValueError("dequantize_cache_packed: format must be 'fp8', 'mxfp4' or 'nvfp4'")
     c = codes.contiguous()
-    if _E4M3 is not None and scales.dtype == _E4M3:       # nvfp4 scale bytes viewed as E4M3
-        scales = scales.view(torch.uint8)
-    s = _as_u8(scales).contiguous()
+    # a typed view of the scale bytes must name the encoding the format stores:
+    # E4M3 bits for nvfp4, E8M0 bytes for mxfp4 and fp8 (raw uint8 is taken as is)
+    if _E4M3 is not None and scales.dtype == _E4M3:
+        if format != "nvfp4":
+            raise TypeError(f"dequantize_cache_packed: float8_e4m3fn scales are nvfp4's; {format} stores E8M0 bytes")
+        s = scales.view(torch.uint8)
+    elif _E8M0 is not None and scales.dtype == _E8M0:
+        if format == "nvfp4":
+            raise TypeError("dequantize_cache_packed: nvfp4 stores E4M3 scale bits, not float8_e8m0fnu")
+        s = scales.view(torch.uint8)
+    elif scales.dtype == torch.uint8:
+        s = scales
+    else:
+        raise TypeError("dequantize_cache_packed: scales must be uint8, float8_e8m0fnu (mxfp4, fp8) "
+                        "or float8_e4m3fn (nvfp4)")
+    s = s.contiguous()
     if c.dtype != torch.uint8 or c.dim() == 0:
         raise TypeError("dequantize_cache_packed: codes must be a uint8 tensor")
     C = c.shape[-1] * (1 if format == "fp8" else 2)

@@ -126,3 +126,26 @@ def test_empty_and_bad_shapes():
         mxq.quantize_cache_packed(torch.zeros(2, 40, dtype=torch.bfloat16, device=dev()), "fp8", 32)
     with pytest.raises(ValueError):
         mxq.quantize_cache_packed(torch.zeros(2, 42, dtype=torch.bfloat16, device=dev()), "nvfp4", 7)
+
+
+def test_typed_scale_views():
+    """nvfp4 scale bytes viewed as float8_e4m3fn, and mxfp4 / fp8 scale bytes
+    viewed as float8_e8m0fnu, decode as the raw bytes do; a view that names
+    the other encoding is refused."""
+    e4m3, e8m0 = getattr(torch, "float8_e4m3fn", None), getattr(torch, "float8_e8m0fnu", None)
+    g = np.random.default_rng(11)
+    bits = random_blocks(g, 24 * 4, 32, "bf16").reshape(24, 128)
+    x = oracle.from_dtype_bits(bits, "bf16")
+    t = to_gpu_bits(bits, "bf16")
+    for fmt, block, view in [("nvfp4", 16, e4m3), ("mxfp4", 32, e8m0), ("fp8", 32, e8m0)]:
+        if view is None:
+            continue
+        wc, ws = oracle.quantize_cache_packed(x, fmt, block)
+        c, s = mxq.quantize_cache_packed(t, fmt, block)
+        back = mxq.dequantize_cache_packed(c, s.view(view), fmt, block, torch.bfloat16)
+        assert_bits_equal(from_gpu_bits(back), oracle.dequantize_cache_packed(wc, ws, fmt, block, "bf16"),
+                          f"{fmt} typed scales")
+        other = e8m0 if view is e4m3 else e4m3
+        if other is not None:
+            with pytest.raises(TypeError):
+                mxq.dequantize_cache_packed(c, s.view(other), fmt, block, torch.bfloat16)
