@@ -666,6 +666,224 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
                       col0 + wave * 64, ndim);
 }
 
+// ------------------------------------------------ forward, whole weight lines
+// BM x 256 tiles (BM = 128 or 96) of 4 waves, two workgroups per CU (their
+// waves share the SIMDs, so one's barrier and memory waits overlap the
+// other's MFMAs), with every weight transfer a whole 128-byte line.  A
+// weight row holds 256 reduction indices (4 steps) per line; a forward that
+// fetches only the 32 bytes of a step makes the L1 move the whole line from
+// L2 each time -- for the routed-expert gate/up projection (7.7 TFLOP) that
+// was 98 GB of L1 <- L2 traffic, two thirds of it weight lines, against 60 GB
+// for a dense bf16 library GEMM of the same shape.  MI355X runs these GEMMs
+// at its board power limit, where the clock, and so the rate, follows the
+// energy spent per flop, and data moved between the caches is a large share
+// of it; with whole lines the traffic falls to 45 GB.
+//  * Activations: two stages of BM x 64 bf16; the stage step s - 1 used
+//    takes step s + 1 right after the barrier that ends step s - 1.
+//  * Weights: each wave owns its 64 columns.  A "generation" of 4 steps (64
+//    columns x 128 bytes, each DMA lane moving 16 bytes of a line, 8 lanes a
+//    whole line; chunk c of column n at c ^ ((n >> 1) & 7)) lands in the
+//    wave's own LDS area; at its first step the wave copies its 32 bytes per
+//    step and column into registers and then fetches the next generation
+//    into the same area, four steps ahead of its use.  No other wave reads
+//    the area, so this needs no barrier.
+//  * Scales: 16 bytes (8 steps) per column, double-buffered per wave.
+// The end of step s waits for exactly this wave's activation transfers of
+// step s + 1 (s_waitcnt vmcnt; the generation and scale chunk issued after
+// them stay in flight), then the barrier publishes every wave's.
+// Needs K % 512 == 0 (whole generations and scale chunks).
+constexpr int kFlBN = 256, kFlThreads = 256;
+
+template <int BM>
+struct FlSmem {
+  uint8_t a[2][BM * 128];              // activation tiles: BM rows x 128 bytes
+  uint8_t b[4][64 * 128];              // weight generation per wave: 64 columns x 128 bytes
+  uint8_t s8[2][kFlBN * 16];           // E8M0 scales: 16 bytes (8 steps) per column
+};
+
+// (the body is a device function template called by one kernel per tile
+// height: clang emitted no host launch stub for it as a kernel template)
+template <int BM>
+__device__ __forceinline__ void fwd_fl_body(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
+                                            const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs,
+                                            int experts, int64_t tokens, int64_t ndim, int64_t kdim,
+                                            uint8_t* __restrict__ out, int gx) {
+  constexpr int BN = kFlBN, MT = BM / 32, NT = 2, QA = BM / 32, kThreads = kFlThreads;   // QA: activation blocks per wave
+  const int64_t col0 = (int64_t)(blockIdx.x % gx) * BN;
+  TileTable<BM> tt;
+  tt.build(offs, experts, tokens);
+  const TileInfo ti = tt.lookup((int)(blockIdx.x / gx));
+  if (ti.expert == -2) return;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, r = lane & 31;
+
+  if (ti.expert == -1) {
+    for (int i = threadIdx.x; i < BM * BN / 8; i += kThreads) {
+      const int rr = i / (BN / 8), c = (i % (BN / 8)) * 8;
+      const int64_t gr = ti.row0 + rr, gc = col0 + c;
+      if (gr < ti.row_end && gc < ndim) {
+        unsigned short* dst = reinterpret_cast<unsigned short*>(out + (gr * ndim + gc) * 2);
+        for (int q = 0; q < 8 && gc + q < ndim; ++q) dst[q] = 0;
+      }
+    }
+    return;
+  }
+
+  __shared__ __attribute__((aligned(1024))) FlSmem<BM> sm;
+
+  // activations: wave w fills blocks QA w .. QA w + QA - 1 of 8 rows (as in the DMA forward)
+  const int64_t prow = kdim / 2, srow = kdim / 32;
+  const __amdgpu_buffer_rsrc_t rs_a = dma_rsrc(a + ti.row0 * kdim * 2, min(ti.row_end - ti.row0, (int64_t)BM) * kdim * 2);
+  uint32_t a_off[QA];
+#pragma unroll
+  for (int q = 0; q < QA; ++q) {
+    const int row = 8 * (QA * wave + q) + (lane >> 3);
+    a_off[q] = (uint32_t)(((int64_t)row * kdim + ((lane & 7) ^ ((row >> 1) & 7)) * 8) * 2);
+  }
+  // this wave's 64 weight columns: block q (q = 0 .. 7) holds columns 8q .. 8q+7,
+  // lane l -> column 8q + l/8, LDS chunk l%8 <- line chunk (l%8) ^ ((column >> 1) & 7)
+  const int64_t n0 = col0 + 64 * wave;
+  const __amdgpu_buffer_rsrc_t rs_b =
+      dma_rsrc(packed_e_of(packed, ti.expert, ndim, kdim) + n0 * prow, (ndim - n0) * prow);
+  // (column 8q + bc: ((8q + bc) >> 1) & 7 = (bc >> 1) ^ 4 (q & 1), so even and odd blocks differ in one swizzle bit)
+  const int bc = lane >> 3;   // column within a block
+  const uint32_t b_off[2] = {(uint32_t)(bc * prow + 16 * ((lane & 7) ^ (bc >> 1))),
+                             (uint32_t)(bc * prow + 16 * ((lane & 7) ^ (bc >> 1) ^ 4))};
+  const uint32_t b_blk = (uint32_t)(8 * prow);   // 8 columns further
+  // scales of this wave's columns: lane l <- column 64 w + l
+  const __amdgpu_buffer_rsrc_t rs_s = dma_rsrc(scales + ((int64_t)ti.expert * ndim + n0) * srow, (ndim - n0) * srow);
+  const uint32_t s_off = (uint32_t)(lane * srow);
+
+  auto issue_a = [&](int step) {
+#pragma unroll
+    for (int q = 0; q < QA; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_void_t*)(sm.a[step & 1] + 1024 * (QA * wave + q)), 16,
+                                               a_off[q], step * kBK * 2, 0, 0);
+  };
+  auto issue_b = [&](int gen) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void_t*)(sm.b[wave] + 1024 * q), 16, b_off[q & 1] + q * b_blk,
+                                               gen * 128, 0, 0);
+  };
+  auto issue_s = [&](int chunk) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void_t*)(sm.s8[chunk & 1] + 1024 * wave), 16, s_off,
+                                             16 * chunk, 0, 0);
+  };
+
+  f32x16_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x16_t{};
+
+  const int nsteps = (int)(kdim / kBK), last = nsteps - 1;   // a multiple of 8
+  const int ngen = nsteps >> 2, nchunk = nsteps >> 3;
+
+  issue_s(0);
+  issue_b(0);
+  issue_a(0);
+  __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);   // vmcnt(0)
+  __syncthreads();
+
+  const uint8_t* bw = sm.b[wave];
+  u32x4_t pw[NT][4];   // the generation's packed bytes: [column tile][step in generation]
+  const int swz_base = r * 128;
+  // t = s % 4, passed as a literal: after inlining it indexes the
+  // generation's registers at compile time
+  auto step = [&](int s, int t) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (t == 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int c = 32 * j + r;
+          pw[j][u] = *reinterpret_cast<const u32x4_t*>(bw + c * 128 + 16 * ((2 * u + h) ^ ((c >> 1) & 7)));
+        }
+    }
+    // the stage step s - 1 used is free (barrier that ended it): step s + 1
+    const bool refill = s + 1 <= last;
+    if (refill) issue_a(s + 1);
+    bool gen_issue = false, chunk_issue = false;
+    if (t == 0) {
+      gen_issue = (s >> 2) + 1 < ngen;
+      chunk_issue = (s & 7) == 0 && (s >> 3) + 1 < nchunk;
+      // the generation's copy has been read before the area is refilled
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      if (gen_issue) issue_b((s >> 2) + 1);
+      if (chunk_issue) issue_s((s >> 3) + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // decode this step's weights into B fragments
+    bf16x8_t fb[NT][4];
+    {
+      const uint8_t* sc_row = sm.s8[(s >> 3) & 1] + 2 * (s & 7) + h;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const float sc = e8m0_to_f32(sc_row[16 * (64 * wave + 32 * j + r)]);
+        const u32x4_t p = pw[j][t];
+        const uint32_t w[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          u32x4_t v = {dec_fp4_bf16x2<0>(w[kk], sc), dec_fp4_bf16x2<1>(w[kk], sc), dec_fp4_bf16x2<2>(w[kk], sc),
+                       dec_fp4_bf16x2<3>(w[kk], sc)};
+          fb[j][kk] = __builtin_bit_cast(bf16x8_t, v);
+        }
+      }
+    }
+    const uint8_t* la = sm.a[s & 1] + swz_base;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int off = 16 * ((4 * h + kk) ^ ((r >> 1) & 7));   // rows 32i + r share the swizzle
+      bf16x8_t fa[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(la + i * 32 * 128 + off);
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j][kk], fa[i], acc[i][j], 0, 0, 0);
+    }
+    if (s == last) return;
+    // step s+1's activations (and everything older) have landed once only the
+    // generation and scale chunk issued after them may be in flight
+    const int pend = (gen_issue ? 8 : 0) + (chunk_issue ? 1 : 0);
+    __builtin_amdgcn_sched_barrier(0);
+    switch (pend) {
+      case 9: wait_vmcnt_barrier<9>(); break;
+      case 8: wait_vmcnt_barrier<8>(); break;
+      case 1: wait_vmcnt_barrier<1>(); break;
+      default: wait_vmcnt_barrier<0>(); break;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (int s = 0; s < nsteps; s += 4) {   // nsteps % 8 == 0
+    step(s, 0);
+    step(s + 1, 1);
+    step(s + 2, 2);
+    step(s + 3, 3);
+  }
+  // nothing is pending after the last step's wait; once every wave is here the LDS is free
+  __syncthreads();
+  static_assert(sizeof(FlSmem<BM>) >= (size_t)4 * BM * 128, "epilogue block fits");
+  store_block_lds<MT>(reinterpret_cast<uint8_t*>(&sm) + wave * BM * 128, acc, lane, out, ndim, ti.row0, ti.row_end,
+                      col0 + 64 * wave, ndim);
+}
+
+__global__ void __launch_bounds__(kFlThreads, 2)
+k_grouped_mm_fwd_fl128(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
+                       const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
+                       int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out, int gx) {
+  fwd_fl_body<128>(a, packed, scales, offs, experts, tokens, ndim, kdim, out, gx);
+}
+__global__ void __launch_bounds__(kFlThreads, 2)
+k_grouped_mm_fwd_fl96(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
+                      const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
+                      int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out, int gx) {
+  fwd_fl_body<96>(a, packed, scales, offs, experts, tokens, ndim, kdim, out, gx);
+}
+
 // ------------------------------------------------------ forward, W4A4
 // y[rows_e] = x_q[rows_e] @ W_e^T with the activations quantized to MXFP4 as
 // well ("NVIDIA Model Optimizer: from mtq.quantize to a 4.95-bit
@@ -1175,13 +1393,22 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
   hipLaunchKernelGGL((k_grouped_mm_fwd_dma<BM, 4, 3, 2, SCH, true>), dim3((unsigned)(NWG)), dim3(kGemmThreads), 0, st, \
                      (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim,      \
                      (uint8_t*)out, (int)gx)
-      if (bm96) {
-        if (sch8) MXQ_FWD_LAUNCH(96, 8, n96);
-        else MXQ_FWD_LAUNCH(96, 2, n96);
+#define MXQ_FL_LAUNCH(BM, NWG)                                                                                   \
+  hipLaunchKernelGGL(k_grouped_mm_fwd_fl##BM, dim3((unsigned)(NWG)), dim3(kFlThreads), 0, st, (const uint8_t*)a,      \
+                     (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim, (uint8_t*)out,       \
+                     (int)gx)
+      // whole weight lines (4 steps per fetch) whenever whole generations and
+      // 16-byte scale chunks exist: 3-5% faster on the routed-expert
+      // projections and ~15% on the 8-expert forward than the per-step form
+      if (sch8) {
+        if (bm96) MXQ_FL_LAUNCH(96, n96);
+        else MXQ_FL_LAUNCH(128, n128);
+      } else if (bm96) {
+        MXQ_FWD_LAUNCH(96, 2, n96);
       } else {
-        if (sch8) MXQ_FWD_LAUNCH(128, 8, n128);
-        else MXQ_FWD_LAUNCH(128, 2, n128);
+        MXQ_FWD_LAUNCH(128, 2, n128);
       }
+#undef MXQ_FL_LAUNCH
 #undef MXQ_FWD_LAUNCH
       return hipGetLastError();
     }
