@@ -53,28 +53,6 @@ struct TileInfo {
   int expert;      // -1: zero-fill slot, -2: nothing to do
 };
 
-// Which expert / row range a row-tile slot covers.
-template <int BM>
-__device__ __forceinline__ TileInfo find_tile(const int32_t* __restrict__ offs, int experts, int64_t tokens,
-                                              int slot) {
-  int64_t start = 0;
-  int acc = 0;
-  for (int e = 0; e < experts; ++e) {
-    // offsets outside [previous, tokens] are clamped into it, so no tile ever
-    // reaches past the activation rows whatever offs holds
-    int64_t end = offs[e];
-    end = end < start ? start : (end > tokens ? tokens : end);
-    const int tiles = (int)((end - start + BM - 1) / BM);
-    if (slot < acc + tiles) return TileInfo{start + (int64_t)(slot - acc) * BM, end, e};
-    acc += tiles;
-    start = end;
-  }
-  // zero-fill slots: rows [offs[E-1], tokens)
-  const int64_t z = start + (int64_t)(slot - acc) * BM;
-  if (z < tokens) return TileInfo{z, tokens, -1};
-  return TileInfo{0, 0, -2};
-}
-
 // Inclusive prefix maximum (MAX) or sum over the 64 lanes of a wave, for
 // values >= 0: a Hillis-Steele scan inside each row of 16 lanes with DPP
 // row shifts (lanes shifted in from outside the row read 0), then each row
@@ -107,7 +85,9 @@ __device__ __forceinline__ int wave_scan(int v) {
 // tiles reach past the slot).  A walk over the offsets (find_tile: a
 // dependent scalar load per expert) measured 2.7-3.0 us per workgroup with
 // 32 experts on MI355X, over half of a forward workgroup's time before its
-// first step.  With more than 64 experts the lookup walks them.
+// first step.  With more than 64 experts the lookup runs the same scans
+// over chunks of 64 experts, carrying the running end and tile count from
+// one chunk to the next, until the chunk holding the slot.
 template <int BM>
 struct TileTable {
   int end;    // lane e < experts: clamped end of expert e's rows; lanes past: the last end
@@ -131,9 +111,39 @@ struct TileTable {
     incl = wave_scan<false>(lane < e_count ? (int)(((int64_t)end - prev + BM - 1) / BM) : 0);
   }
 
-  // the same result as find_tile<BM>(offs, experts, tokens, slot); every lane active
+  // more than 64 experts: chunk c of the experts is scanned as build() scans
+  // the first 64, its ends offset by the running end of the chunks before
+  // (a running maximum) and its tile counts by their total
+  __device__ __forceinline__ TileInfo lookup_chunked(int slot) const {
+    const int lane = threadIdx.x & 63;
+    int run_end = 0, run_tiles = 0;
+    for (int c0 = 0; c0 < experts; c0 += 64) {
+      const int n = min(experts - c0, 64);
+      const int v = wave_scan<true>(lane < n ? max(offs[c0 + lane], 0) : 0);
+      const int e_end = (int)min((int64_t)max(v, run_end), tokens);
+      int prev = __shfl_up(e_end, 1);
+      if (lane == 0) prev = run_end;
+      const int inc = run_tiles + wave_scan<false>(lane < n ? (int)(((int64_t)e_end - prev + BM - 1) / BM) : 0);
+      const uint64_t live = n == 64 ? ~0ull : ((1ull << n) - 1);
+      const uint64_t m = __ballot(inc > slot) & live;
+      if (m) {
+        const int e = __builtin_ctzll(m);
+        const int before = e ? __builtin_amdgcn_readlane(inc, e - 1) : run_tiles;
+        const int start = e ? __builtin_amdgcn_readlane(e_end, e - 1) : run_end;
+        return TileInfo{start + (int64_t)(slot - before) * BM, __builtin_amdgcn_readlane(e_end, e), c0 + e};
+      }
+      run_end = __builtin_amdgcn_readlane(e_end, n - 1);
+      run_tiles = __builtin_amdgcn_readlane(inc, n - 1);
+    }
+    const int64_t z = run_end + (int64_t)(slot - run_tiles) * BM;
+    if (z < tokens) return TileInfo{z, tokens, -1};
+    return TileInfo{0, 0, -2};
+  }
+
+  // which expert and row range a row-tile slot covers (-1: rows no expert
+  // owns, to be zeroed; -2: nothing to do); every lane active
   __device__ __forceinline__ TileInfo lookup(int slot) const {
-    if (experts > 64) return find_tile<BM>(offs, experts, tokens, slot);
+    if (experts > 64) return lookup_chunked(slot);
     const uint64_t live = experts == 64 ? ~0ull : ((1ull << experts) - 1);
     const uint64_t m = __ballot(incl > slot) & live;
     if (m) {

@@ -268,3 +268,37 @@ def test_moe_layer_workload_sampled_rows():
             print(f"{name} {what}: sampled rel Frobenius {err:.2e}")
             assert err <= TOL, f"{name} {what}: {err:.3e}"
         del y, gx
+
+
+@pytest.mark.parametrize("E,clamp", [(96, False), (256, False), (96, True), (256, True)])
+def test_many_experts(E, clamp):
+    """More than 64 experts: the tile lookup scans the offsets 64 experts at a
+    time.  Forward, grad_x and the W4A4 forward against the oracle, with empty
+    experts, rows no expert owns and (clamp) offsets that go negative,
+    decrease and pass the row count, which the kernels clamp into
+    [previous clamped offset, tokens]."""
+    T, N, K = 6000, 256, 512
+    g = np.random.default_rng(E + clamp)
+    counts = g.integers(0, 2 * T // E, E)
+    counts[g.choice(E, E // 8, replace=False)] = 0
+    raw = np.cumsum(counts)
+    raw = (raw * (T - 37) // max(int(raw[-1]), 1)).astype(np.int64)      # 37+ uncovered rows
+    if clamp:
+        idx = g.choice(E, 12, replace=False)
+        raw[idx[:4]] = -7
+        raw[idx[4:8]] = raw[idx[4:8]] // 2
+        raw[idx[8:]] = T + 1000
+    raw = raw.astype(np.int32)
+    offs = np.minimum(np.maximum.accumulate(np.maximum(raw, 0)), T).astype(np.int32)
+    packed, scales, xb = random_case(E * 13 + clamp, E, T, N, K, offs)
+    pt, st = gpu_weights(packed, scales)
+    ot = torch.from_numpy(raw).to(dev())
+    x = oracle.from_dtype_bits(xb, "bf16")
+    y = mxq.mxfp4_grouped_mm_fwd(to_gpu_bits(xb, "bf16"), pt, st, ot)
+    check_segments(bf16_values(y), oracle.grouped_mm_fwd(x, packed, scales, offs), offs, what=f"E={E} fwd")
+    gb = synth.normal_bf16(np.random.default_rng(E), (T, N), 0.1)
+    gx = mxq.mxfp4_grouped_mm_bwd_x(to_gpu_bits(gb, "bf16"), pt, st, ot)
+    want_b = oracle.grouped_mm_bwd_x(oracle.from_dtype_bits(gb, "bf16"), packed, scales, offs)
+    check_segments(bf16_values(gx), want_b, offs, what=f"E={E} bwd_x")
+    y4 = mxq.mxfp4_grouped_mm_fwd_w4a4(to_gpu_bits(xb, "bf16"), pt, st, ot)
+    check_segments(bf16_values(y4), oracle.grouped_mm_fwd_w4a4(x, packed, scales, offs), offs, what=f"E={E} w4a4")
