@@ -104,7 +104,7 @@ def main():
     t_gen = time.perf_counter()
 
     # ---------------- routed-expert layer (gate/up + down, fwd + grad_x)
-    moe = None
+    moe = bulk = kv = None
     if wanted("moe") or wanted("w4a4"):
         moe = synth.moe_layer(seed=0)
         T = int(moe["offs"][-1])
@@ -335,10 +335,22 @@ def main():
     moe_flop = sum(l.work for l in moe_legs)
     moe_ms = sum(l.ms for l in moe_legs) / K
     value = moe_flop / (moe_ms * 1e-3) / 1e12 if moe_ms > 0 else None
+    # HBM aggregates: the quantize/dequantize and fake-quant cache rows of the
+    # path (mxfp4 codec, quantize_cache and its straight-through copy, weight
+    # dequant), and separately the rows built beyond them (packed KV storage,
+    # two-level NVFP4)
+    def is_next(l):
+        return l.name.startswith(("kv.pack", "kv.unpack")) or "nvfp4" in l.name.split(".")[1] and not \
+            l.name.startswith(("kv.quantize_cache", "bulk.quantize_cache"))
+
+    def aggregate(ls):
+        b = sum(l.work * l.reps for l in ls)
+        ms = sum(l.ms for l in ls) / K
+        return b / (ms * 1e-3) / 1e9 if ms > 0 else None
+
     codec = [l for l in legs if l.kind == "byte" and not l.alu_ops and not l.name.startswith(("roundtrip", "w4a4."))]
-    codec_bytes = sum(l.work * l.reps for l in codec)
-    codec_ms = sum(l.ms for l in codec) / K
-    hbm_gbps = codec_bytes / (codec_ms * 1e-3) / 1e9 if codec_ms > 0 else None
+    hbm_gbps = aggregate([l for l in codec if not is_next(l)])
+    hbm_next_gbps = aggregate([l for l in codec if is_next(l)])
 
     # dominant kernel: the instantiation with the largest total event time
     by_kernel = {}
@@ -363,6 +375,8 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and moe is not None:
         cpu = cpu_baseline(moe)
+        cpu["codecs"] = cpu_baseline_codecs(bulk_x=bulk["x"] if bulk is not None else None,
+                                            kv_x=kv["x"] if kv is not None else None)
 
     line = {
         "metric": METRIC,
@@ -387,7 +401,11 @@ def main():
         },
         "hbm": {"GB/s": round(hbm_gbps, 1) if hbm_gbps else None,
                 "frac": round(hbm_gbps / HBM_PEAK_GBPS, 4) if hbm_gbps else None,
-                "legs": "codec legs: kv + bulk"},
+                "legs": "quantize_mxfp4 / dequantize_mxfp4 / quantize_cache (fp8, mxfp4, nvfp4) / STE copy / "
+                        "weight dequant legs (kv + bulk)"},
+        "hbm_next": {"GB/s": round(hbm_next_gbps, 1) if hbm_next_gbps else None,
+                     "frac": round(hbm_next_gbps / HBM_PEAK_GBPS, 4) if hbm_next_gbps else None,
+                     "legs": "packed KV store/load and two-level NVFP4 quantize/dequantize legs"},
         "mfma": {"TFLOP/s": round(value, 1) if value else None,
                  "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4) if value else None},
         "w4a4": w4a4_summary(legs, K),
@@ -465,6 +483,54 @@ def cpu_baseline(moe):
             "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"gate/up forward, 1024 rows x {len(experts)} experts (float64 dequant + BLAS matmul), "
                       f"{flop / 1e9:.0f} GFLOP in {dt:.1f} s"}
+
+
+def cpu_baseline_codecs(bulk_x=None, kv_x=None):
+    """The oracle's quantize / dequantize / quantize_cache (NumPy, one thread,
+    unmodified) on row samples of the bulk bf16 [65536, 7168] activation and
+    the bf16 [4, 8192, 512] KV cache; GB/s counts the same algorithmic bytes
+    as the GPU legs."""
+    import numpy as np
+    import oracle
+    import synth
+    out = []
+    cores = 1   # NumPy elementwise code runs on one thread
+
+    def timed(name, fn, nbytes, sample, min_s=0.5):
+        reps, t = 0, 0.0
+        t0 = time.perf_counter()
+        while t < min_s:
+            fn()
+            reps += 1
+            t = time.perf_counter() - t0
+        out.append({"name": name, "GB/s": round(nbytes * reps / t / 1e9, 4), "s_per_call": round(t / reps, 3),
+                    "cores": cores, "kind": "oracle", "sample": sample})
+
+    if bulk_x is None:
+        bulk_x = synth.bulk_stream(seed=0)["x"]
+    rows = 128
+    xb = np.ascontiguousarray(bulk_x[:rows])
+    n = xb.size
+    sample = f"rows 0..{rows - 1} of the bf16 [65536, 7168] activation ({n} elements)"
+    xf = oracle.from_dtype_bits(xb, "bf16")
+    packed, scales = oracle.quantize_mxfp4(xf)
+    timed("bulk.quantize_mxfp4", lambda: oracle.quantize_mxfp4(oracle.from_dtype_bits(xb, "bf16")),
+          n * (2 + 0.5 + 1 / 32), sample)
+    timed("bulk.dequantize_mxfp4", lambda: oracle.dequantize_mxfp4(packed, scales, "bf16"), n * (0.5 + 1 / 32 + 2),
+          sample)
+    for fmt, block in [("nvfp4", 16), ("fp8", 128), ("mxfp4", 32)]:
+        timed(f"bulk.quantize_cache.{fmt}",
+              lambda fmt=fmt, block=block: oracle.quantize_cache(oracle.from_dtype_bits(xb, "bf16"), fmt, block,
+                                                                 "bf16"), 4.0 * n, sample)
+    kv = (kv_x if kv_x is not None else synth.kv_cache(seed=0)["x"]).reshape(-1, 512)
+    kvs = np.ascontiguousarray(kv[:2048])
+    nk = kvs.size
+    ksample = f"rows 0..2047 (of 32768) of the bf16 [4, 8192, 512] KV cache ({nk} elements)"
+    for fmt, block in [("fp8", 128), ("mxfp4", 32), ("nvfp4", 16)]:
+        timed(f"kv.quantize_cache.{fmt}",
+              lambda fmt=fmt, block=block: oracle.quantize_cache(oracle.from_dtype_bits(kvs, "bf16"), fmt, block,
+                                                                 "bf16"), 4.0 * nk, ksample)
+    return out
 
 
 if __name__ == "__main__":
