@@ -23,7 +23,7 @@ Sources (page title, then the section on that page):
   cast, the E4M3 range 448 and smallest scale 2^-9, packing expression, and
   the two-level NVFP4 format of ``oracle/nvfp4.py``); section "Where the
   scales come from" (the MSE block-scale sweep); section "The claims,
-  marked reported" (W4A4).
+  marked reported" (W4A4 and W4A8).
 
 Every function is pinned by tests under ``tests/test_oracle_*.py`` against facts
 the pages print, closed forms, invariants, library routines for special cases
@@ -50,7 +50,7 @@ from .nvfp4 import (global_scale as nvfp4_global_scale, e4m3_bits, e4m3_decode, 
                     quantize_nvfp4, dequantize_nvfp4_values, dequantize_nvfp4, block_sq_errors as nvfp4_block_sq_errors,
                     mse_block_scales as nvfp4_mse_block_scales, quantize_nvfp4_mse)
 from .grouped_mm import (dequantize_expert_weights, grouped_mm_fwd, grouped_mm_bwd_x, grouped_mm_rows, segments,
-                         w4a4_activations, grouped_mm_fwd_w4a4)
+                         w4a4_activations, grouped_mm_fwd_w4a4, w4a8_activations, grouped_mm_fwd_w4a8)
 
 __all__ = [
     "E2M1_TABLE", "E2M1_MIDPOINTS", "MXFP4_BLOCK_SIZE", "E4M3_MAX",
@@ -60,7 +60,7 @@ __all__ = [
     "power_of_two_ceiling", "cache_scale", "quantize_cache", "quantize_cache_backward",
     "quantize_cache_packed", "dequantize_cache_packed",
     "dequantize_expert_weights", "grouped_mm_fwd", "grouped_mm_bwd_x", "grouped_mm_rows", "segments",
-    "w4a4_activations", "grouped_mm_fwd_w4a4",
+    "w4a4_activations", "grouped_mm_fwd_w4a4", "w4a8_activations", "grouped_mm_fwd_w4a8",
     "nvfp4_global_scale", "e4m3_bits", "e4m3_decode", "nvfp4_encode", "quantize_nvfp4", "dequantize_nvfp4_values",
     "dequantize_nvfp4", "nvfp4_block_sq_errors", "nvfp4_mse_block_scales", "quantize_nvfp4_mse",
 ]

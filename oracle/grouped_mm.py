@@ -16,6 +16,8 @@ Test infrastructure only (see ``oracle/__init__.py``).  float64 throughout.
 import numpy as np
 
 from .mxfp4 import dequantize_mxfp4_values, quantize_mxfp4
+from .cache import quantize_cache_packed
+from .nvfp4 import e4m3_decode
 
 
 def segments(offs, tokens):
@@ -107,6 +109,33 @@ def grouped_mm_fwd_w4a4(x, packed, scales, offs, rows=None):
     round trip of ``w4a4_activations``, then ``grouped_mm_fwd`` on those
     exact values (float64).  ``rows`` as in ``grouped_mm_fwd``."""
     return grouped_mm_fwd(w4a4_activations(x), packed, scales, offs, rows=rows)
+
+
+def w4a8_activations(x):
+    """Exact float64 values of activations x [T, K] after fp8 quantization:
+    E4M3 codes with one E8M0 power-of-two scale per 32 consecutive columns,
+    the form ``quantize_cache_packed(x, "fp8", 32)`` stores (scale = power-of-
+    two ceiling of fl32(amax / 448), floored at 2^-126; elements rounded to
+    E4M3 nearest-even).
+
+    Reading: "NVIDIA Model Optimizer: from mtq.quantize to a 4.95-bit
+    DeepSeek-R1", section "NVFP4 in the code: two scales and a nibble", has
+    activation scales computed at run time, and its "The claims, marked
+    reported" section names W4A8 beside W4A4 among the weight-and-activation
+    forms; the pages define one fp8 activation encoding with power-of-two
+    block scales, the fp8 form of "nemo_automodel.components.models.
+    deepseek_v41.quantization" quantize_cache, taken here at the 32-column
+    block of the MXFP4 weights (the block the block-scaled MFMA scales by).
+    Each row is independent, so a subset of rows can be quantized alone."""
+    codes, sc = quantize_cache_packed(np.asarray(x, dtype=np.float64), "fp8", 32)
+    return e4m3_decode(codes) * np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 32, axis=-1)
+
+
+def grouped_mm_fwd_w4a8(x, packed, scales, offs, rows=None):
+    """W4A8 forward: y[rows_e] = q8(x)[rows_e] @ W_e^T, with q8 the fp8
+    round trip of ``w4a8_activations``, then ``grouped_mm_fwd`` on those
+    exact values (float64).  ``rows`` as in ``grouped_mm_fwd``."""
+    return grouped_mm_fwd(w4a8_activations(x), packed, scales, offs, rows=rows)
 
 
 def grouped_mm_rows(rows, packed, scales, offs, x_rows=None, g_rows=None):

@@ -206,3 +206,91 @@ def test_w4a4_on_grid_values_is_the_plain_forward():
                           oracle.grouped_mm_fwd(xg, packed, scales, offs))
     assert not np.allclose(oracle.grouped_mm_fwd_w4a4(x0, packed, scales, offs),
                            oracle.grouped_mm_fwd(x0, packed, scales, offs))
+
+
+# ----------------------------------------------------------------- W4A8
+def _e4m3_grid():
+    """All non-negative finite E4M3 (FN) values with their codes: subnormals
+    m * 2^-9, normals (1 + m/8) * 2^(e-7), e = 1..15, without (15, 7) (NaN)."""
+    vals = [(m * 2.0 ** -9, m) for m in range(8)]
+    vals += [((1 + m / 8) * 2.0 ** (e - 7), (e << 3) | m) for e in range(1, 16) for m in range(8) if (e, m) != (15, 7)]
+    return vals
+
+
+def _brute_fp8_value(v, s):
+    """v / s rounded to the nearest E4M3 value (ties to the even code) times s."""
+    q = abs(v) / s
+    best = min(_e4m3_grid(), key=lambda gc: (abs(q - gc[0]), gc[1] % 2))
+    return (-1.0 if v < 0 else 1.0) * best[0] * s
+
+
+def _brute_ceil_scale(amax):
+    """Smallest power of two >= fl32(amax / 448), at least 2^-126, by search."""
+    r = float(np.float32(np.float32(amax) / np.float32(448.0)))
+    j = -126
+    while 2.0 ** j < r:
+        j += 1
+    return 2.0 ** j
+
+
+def test_w4a8_matches_brute_force():
+    """Per-element scalar fp8 quantization (scale by search, nearest E4M3
+    value with ties to the even code, subnormals included) and an explicit
+    triple loop, on 2 experts."""
+    g = np.random.default_rng(15)
+    E, T, N, K = 2, 5, 3, 64
+    packed, scales = rand_weights(g, E, N, K)
+    x = g.standard_normal((T, K)) * np.repeat(2.0 ** g.integers(-30, 30, size=(T, K // 32)), 32, axis=1)
+    # ties of the E4M3 grid (midpoints between neighbours, 1.0625 = 1 + 1/16)
+    # under a block maximum 448 that fixes the scale at 1
+    x[0, :32] = np.tile([448.0, 1.0625, 1.1875, 3.0 * 2.0 ** -10, 0.5 * 2.0 ** -9, 9.0, 17.0, 240.0], 4)
+    x[1, 32:] = 0.0                                          # an all-zero block
+    x[2, :32] *= 2.0 ** -140                                 # tiny block: the 2^-126 floor
+    offs = np.array([2, 5], np.int32)
+    y = oracle.grouped_mm_fwd_w4a8(x, packed, scales, offs)
+    for t in range(T):
+        e_t = 0 if t < 2 else 1
+        xv = []
+        for b in range(K // 32):
+            blk = x[t, 32 * b:32 * b + 32]
+            s = _brute_ceil_scale(max(abs(v) for v in blk))
+            xv += [_brute_fp8_value(v, s) for v in blk]
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                byte = int(packed[e_t, n, k // 2]) & 0xFF
+                nib = byte & 0xF if k % 2 == 0 else byte >> 4
+                w = (-1.0 if nib & 8 else 1.0) * _GRID[nib & 7] * 2.0 ** (int(scales[e_t, n, k // 32]) - 127)
+                acc += xv[k] * w
+            assert abs(y[t, n] - acc) <= 1e-12 * max(1.0, abs(acc)), (t, n, y[t, n], acc)
+
+
+def test_w4a8_activations_are_the_fp8_cache_round_trip():
+    """The activations equal quantize_cache's fp8 fake-quant at block 32
+    (the values its packed form decodes to), and sit within half an E4M3
+    step of x: |q - x| <= 2^-4 |x| for normal values, <= 2^-10 s below."""
+    g = np.random.default_rng(16)
+    x = g.standard_normal((64, 256)) * np.repeat(2.0 ** g.integers(-20, 20, size=(64, 8)), 32, axis=1)
+    q = oracle.w4a8_activations(x)
+    assert np.array_equal(q, oracle.cache.quantize_cache_values(x, "fp8", 32))
+    s = np.repeat(oracle.cache_scale(np.max(np.abs(x.reshape(64, 8, 32)), axis=-1), "fp8"), 32, axis=1)
+    normal = np.abs(x) >= 2.0 ** -6 * s
+    assert np.all(np.abs(q - x)[normal] <= 2.0 ** -4 * np.abs(x)[normal])
+    assert np.all(np.abs(q - x)[~normal] <= 2.0 ** -10 * s[~normal])
+
+
+def test_w4a8_on_grid_values_is_the_plain_forward():
+    """Activations already on the fp8 grid (one round trip) are fixed points
+    of the quantizer, so the W4A8 forward equals the plain forward exactly;
+    off-grid activations do not."""
+    g = np.random.default_rng(17)
+    E, T, N, K = 3, 40, 16, 128
+    packed, scales = rand_weights(g, E, N, K)
+    offs = np.array([10, 10, 33], np.int32)
+    x0 = g.standard_normal((T, K))
+    xg = oracle.w4a8_activations(x0)
+    assert np.array_equal(oracle.w4a8_activations(xg), xg)
+    assert np.array_equal(oracle.grouped_mm_fwd_w4a8(xg, packed, scales, offs),
+                          oracle.grouped_mm_fwd(xg, packed, scales, offs))
+    assert not np.allclose(oracle.grouped_mm_fwd_w4a8(x0, packed, scales, offs),
+                           oracle.grouped_mm_fwd(x0, packed, scales, offs))
