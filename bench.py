@@ -40,6 +40,7 @@ import time
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 MFMA_FP4_PEAK_TFLOPS = 10100.0   # MI355X dense fp4 (MXFP4) MFMA
+MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 # fp32 VALU issue rate without packed (two-wide) fp32 or FMA pairing: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 ALU_FP32_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 METRIC = "quant/dequant GB/s (% HBM peak); MXFP4 grouped-GEMM TFLOP/s (% MFMA peak)"
@@ -105,7 +106,7 @@ def main():
 
     # ---------------- routed-expert layer (gate/up + down, fwd + grad_x)
     moe = bulk = kv = None
-    if wanted("moe") or wanted("w4a4"):
+    if wanted("moe") or wanted("w4a4") or wanted("w4a8"):
         moe = synth.moe_layer(seed=0)
         T = int(moe["offs"][-1])
         E, H, I2, I = 32, 7168, 4096, 2048
@@ -162,6 +163,34 @@ def main():
                     quant(h, I, dn_xq, dn_xs)),
                 Leg("w4a4.down.fwd", "k_grouped_mm_fwd_w4a4", "flop", 2.0 * moe_rows * H * I,
                     w4(dn_xq, dn_xs, dn_p, dn_s, H, I, dn_y), peak=MFMA_FP4_PEAK_TFLOPS),
+            ]
+
+        # the same forwards as W4A8: the activations encoded as E4M3 with E8M0
+        # block-32 scales (quantize_cache_packed, fp8), then the fp8 x fp4 GEMM
+        if wanted("w4a8"):
+            gu_x8 = torch.empty(T, H, dtype=torch.uint8, device=dev)
+            gu_s8 = torch.empty(T, H // 32, dtype=torch.uint8, device=dev)
+            dn_x8 = torch.empty(T, I, dtype=torch.uint8, device=dev)
+            dn_s8 = torch.empty(T, I // 32, dtype=torch.uint8, device=dev)
+
+            def enc8(a, k, xq, xs):
+                return lambda i: check(L.quantize_cache_packed(a.data_ptr(), mxq._lib.MXQ_BF16, T, k, mxq._lib.MXQ_FMT_FP8,
+                                                               32, xq.data_ptr(), xs.data_ptr(), sp), "encode x fp8")
+
+            def w8(xq, xs, p, s, n, k, y):
+                return lambda i: check(L.mxfp4_grouped_mm_fwd_w4a8(xq.data_ptr(), xs.data_ptr(), T, k, p.data_ptr(),
+                                                                   s.data_ptr(), E, n, offs.data_ptr(), y.data_ptr(),
+                                                                   sp), "w4a8 fwd")
+
+            legs += [
+                Leg("w4a8.gate_up.quantize_x", "k_quantize_cache_packed<bf16,fp8,4>", "byte", T * H * (2 + 1 + 1 / 32),
+                    enc8(x_routed, H, gu_x8, gu_s8)),
+                Leg("w4a8.gate_up.fwd", "k_grouped_mm_fwd_w4a8", "flop", 2.0 * moe_rows * I2 * H,
+                    w8(gu_x8, gu_s8, gu_p, gu_s, I2, H, gu_y), peak=MFMA_FP8_PEAK_TFLOPS),
+                Leg("w4a8.down.quantize_x", "k_quantize_cache_packed<bf16,fp8,4>", "byte", T * I * (2 + 1 + 1 / 32),
+                    enc8(h, I, dn_x8, dn_s8)),
+                Leg("w4a8.down.fwd", "k_grouped_mm_fwd_w4a8", "flop", 2.0 * moe_rows * H * I,
+                    w8(dn_x8, dn_s8, dn_p, dn_s, H, I, dn_y), peak=MFMA_FP8_PEAK_TFLOPS),
             ]
 
     # ---------------- 8-expert grouped GEMM forward (4 rotating buffer sets > 256 MB)
@@ -348,7 +377,7 @@ def main():
         ms = sum(l.ms for l in ls) / K
         return b / (ms * 1e-3) / 1e9 if ms > 0 else None
 
-    codec = [l for l in legs if l.kind == "byte" and not l.alu_ops and not l.name.startswith(("roundtrip", "w4a4."))]
+    codec = [l for l in legs if l.kind == "byte" and not l.alu_ops and not l.name.startswith(("roundtrip", "w4a4.", "w4a8."))]
     hbm_gbps = aggregate([l for l in codec if not is_next(l)])
     hbm_next_gbps = aggregate([l for l in codec if is_next(l)])
 
@@ -395,7 +424,7 @@ def main():
             "workload": "routed-expert layer share (32 experts, hidden 7168, intermediate 2048, 131072 routed rows, "
                         "fwd + grad_x) + 8-expert GEMM [4096x4096 -> 2048] + bf16 KV cache [4,8192,512] fake-quant "
                         "fp8/128, mxfp4/32, nvfp4/16 + STE + packed KV store/load + bulk bf16 [65536,7168] codecs (mxfp4, two-level nvfp4, "
-                        "cache fake-quant) + NVFP4 MSE scale sweep of a bf16 [4096,7168] weight + [64,4096,4096] weight dequant + W4A4 routed-expert forwards",
+                        "cache fake-quant) + NVFP4 MSE scale sweep of a bf16 [4096,7168] weight + [64,4096,4096] weight dequant + W4A4 and W4A8 routed-expert forwards",
             "value_is": "grouped-GEMM TFLOP/s of the routed-expert layer legs (event time)",
             "moe_rows": moe_rows,
         },
@@ -408,7 +437,8 @@ def main():
                      "legs": "packed KV store/load and two-level NVFP4 quantize/dequantize legs"},
         "mfma": {"TFLOP/s": round(value, 1) if value else None,
                  "frac": round(value / MFMA_BF16_PEAK_TFLOPS, 4) if value else None},
-        "w4a4": w4a4_summary(legs, K),
+        "w4a4": low_bit_summary(legs, K, "w4a4", MFMA_FP4_PEAK_TFLOPS),
+        "w4a8": low_bit_summary(legs, K, "w4a8", MFMA_FP8_PEAK_TFLOPS),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "legs": out_legs,
@@ -417,22 +447,23 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def w4a4_summary(legs, K):
-    """The routed-expert forwards as W4A4: GEMM rate against the fp4 peak, and
-    the rate with the activation quantization counted in."""
-    g = [l for l in legs if l.name.startswith("w4a4.") and l.kind == "flop"]
-    q = [l for l in legs if l.name.startswith("w4a4.") and l.kind == "byte"]
+def low_bit_summary(legs, K, prefix, peak):
+    """The routed-expert forwards as W4A4 or W4A8: GEMM rate against the fp4
+    or fp8 peak, and the rate with the activation quantization counted in."""
+    g = [l for l in legs if l.name.startswith(prefix + ".") and l.kind == "flop"]
+    q = [l for l in legs if l.name.startswith(prefix + ".") and l.kind == "byte"]
     if not g:
         return None
     flop = sum(l.work for l in g)
     g_ms, q_ms = sum(l.ms for l in g) / K, sum(l.ms for l in q) / K
     bf = [l for l in legs if l.name in ("moe.gate_up.fwd", "moe.down.fwd")]
     bf_ms = sum(l.ms for l in bf) / K
+    enc = "quantize_mxfp4" if prefix == "w4a4" else "quantize_cache_packed fp8/32"
     return {"gemm_TFLOP/s": round(flop / (g_ms * 1e-3) / 1e12, 1),
-            "frac_fp4": round(flop / (g_ms * 1e-3) / 1e12 / MFMA_FP4_PEAK_TFLOPS, 4),
+            "frac_peak": round(flop / (g_ms * 1e-3) / 1e12 / peak, 4), "peak_TFLOP/s": peak,
             "with_quantize_TFLOP/s": round(flop / ((g_ms + q_ms) * 1e-3) / 1e12, 1),
             "speedup_vs_bf16_fwd": round(bf_ms / (g_ms + q_ms), 3) if len(bf) == 2 else None,
-            "legs": "w4a4.gate_up + w4a4.down forwards (quantize_mxfp4 of the activations + fp4 MFMA GEMM)"}
+            "legs": f"{prefix}.gate_up + {prefix}.down forwards ({enc} of the activations + block-scaled MFMA GEMM)"}
 
 
 def measured_traffic(kernel):

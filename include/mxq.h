@@ -245,6 +245,30 @@ int mxfp4_grouped_mm_fwd_w4a4(const int8_t* xq, const uint8_t* xs, int64_t token
                               const int8_t* packed, const uint8_t* scales, int64_t experts, int64_t n,
                               const int32_t* offs, void* y, void* stream);
 
+/*
+ * mxfp4_grouped_mm_fwd_w4a8 -- the forward with the activations in fp8 (W4A8;
+ * [MO] section "NVFP4 in the code: two scales and a nibble": activation
+ * scales are computed at run time; section "The claims, marked reported"
+ * names W4A8 among the weight-and-activation forms).
+ * xq uint8 [tokens, k] are E4M3 (FN) codes and xs uint8 [tokens, k/32] their
+ * E8M0 block scales, one per 32 consecutive k, as quantize_cache_packed
+ * writes them for format fp8 and block_size 32 ([QC] quantize_cache: scale =
+ * power-of-two ceiling of amax / 448); weights and offs as in
+ * mxfp4_grouped_mm_fwd.  Computes y[rows_e] = dq(xq)[rows_e] @ dq(W_e)^T into
+ * y bf16 [tokens, n] on the block-scaled MFMA (fp8 x fp4): products of codes
+ * and scales are exact, sums run in fp32, the output rounds nearest-even;
+ * rows past offs[experts-1] are written as zeros, offsets are clamped as in
+ * the forward.  A scale byte 0xFF, or an E4M3 NaN code, makes the products it
+ * scales NaN.
+ * Needs k % 512 == 0 and k < 2^22, n % 8 == 0, one expert's packed weights
+ * below 2 GiB (n * k / 2 < 2^31), else MXQ_ERR_SHAPE; xq, xs, packed, scales
+ * and y 16-byte aligned, else MXQ_ERR_ALIGN; y must not overlap xq or xs
+ * (MXQ_ERR_ALIAS).  MXQ_ERR_HIP past 2^23 output tiles of 96 x 256.
+ */
+int mxfp4_grouped_mm_fwd_w4a8(const uint8_t* xq, const uint8_t* xs, int64_t tokens, int64_t k,
+                              const int8_t* packed, const uint8_t* scales, int64_t experts, int64_t n,
+                              const int32_t* offs, void* y, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* mxq_status_string(int status);
 

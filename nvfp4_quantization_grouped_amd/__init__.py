@@ -17,6 +17,8 @@ from .ops import (
     mxfp4_grouped_mm_fwd,
     mxfp4_grouped_mm_fwd_w4a4,
     mxfp4_grouped_mm_fwd_w4a4_quantized,
+    mxfp4_grouped_mm_fwd_w4a8,
+    mxfp4_grouped_mm_fwd_w4a8_quantized,
     quantize_cache,
     quantize_cache_bwd,
     quantize_cache_forward,
@@ -32,6 +34,7 @@ __all__ = [
     "MXFP4_BLOCK_SIZE", "CacheQuantization", "MXFP4GroupedMM",
     "dequantize_mxfp4", "mxfp4_grouped_mm_bwd_x", "mxfp4_grouped_mm_fwd",
     "mxfp4_grouped_mm_fwd_w4a4", "mxfp4_grouped_mm_fwd_w4a4_quantized",
+    "mxfp4_grouped_mm_fwd_w4a8", "mxfp4_grouped_mm_fwd_w4a8_quantized",
     "quantize_cache", "quantize_cache_bwd", "quantize_cache_forward", "quantize_mxfp4",
     "quantize_nvfp4", "dequantize_nvfp4", "quantize_cache_packed", "dequantize_cache_packed",
     "quantize_nvfp4_mse",

@@ -212,11 +212,30 @@ int mxfp4_grouped_mm_fwd_w4a4(const int8_t* xq, const uint8_t* xs, int64_t token
       mxq::launch_grouped_mm_w4a4(xq, xs, tokens, packed, scales, experts, n, k, offs, y, (hipStream_t)stream));
 }
 
+int mxfp4_grouped_mm_fwd_w4a8(const uint8_t* xq, const uint8_t* xs, int64_t tokens, int64_t k, const int8_t* packed,
+                              const uint8_t* scales, int64_t experts, int64_t n, const int32_t* offs, void* y,
+                              void* stream) {
+  if (tokens < 0 || k < 0 || n < 0 || experts < 0) return MXQ_ERR_SHAPE;
+  // whole 16-byte scale chunks per row; 32-bit buffer offsets into one expert's weights
+  if (k % 512 != 0 || n % 8 != 0 || k >= (int64_t(1) << 22) || n * (k / 2) >= (int64_t(1) << 31)) return MXQ_ERR_SHAPE;
+  if (tokens > 0 && n > 0 && (!y || (k > 0 && (!xq || !xs)) || (k > 0 && experts > 0 && (!packed || !scales || !offs))))
+    return MXQ_ERR_NULL;
+  if (((uintptr_t)xq & 15) || ((uintptr_t)xs & 15) || ((uintptr_t)packed & 15) || ((uintptr_t)scales & 15) ||
+      ((uintptr_t)y & 15))
+    return MXQ_ERR_ALIGN;
+  const int64_t ybytes = tokens * n * 2;
+  if (overlap(xq, tokens * k, y, ybytes) || overlap(xs, tokens * (k / 32), y, ybytes)) return MXQ_ERR_ALIAS;
+  if (tokens == 0 || n == 0) return MXQ_OK;
+  if (k == 0 || experts == 0) return from_hip(mxq::launch_zero(y, ybytes, (hipStream_t)stream));
+  return from_hip(
+      mxq::launch_grouped_mm_w4a8(xq, xs, tokens, packed, scales, experts, n, k, offs, y, (hipStream_t)stream));
+}
+
 const char* mxq_status_string(int s) {
   switch (s) {
     case MXQ_OK: return "ok";
     case MXQ_ERR_NULL: return "null pointer";
-    case MXQ_ERR_SHAPE: return "bad shape (negative size, k not a multiple of the block (32 mxfp4, 16 nvfp4, 512 W4A4), n not a multiple of 8, or past a size limit)";
+    case MXQ_ERR_SHAPE: return "bad shape (negative size, k not a multiple of the block (32 mxfp4, 16 nvfp4, 512 W4A4 and W4A8), n not a multiple of 8, or past a size limit)";
     case MXQ_ERR_DTYPE: return "unsupported dtype";
     case MXQ_ERR_FORMAT: return "unknown format (fp8, mxfp4 or nvfp4)";
     case MXQ_ERR_BLOCK: return "block_size must be positive";

@@ -773,8 +773,8 @@ __device__ __forceinline__ void fwd_fl_body(const uint8_t* __restrict__ a, const
   auto issue_b = [&](int gen) {
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void_t*)(sm.b[wave] + 1024 * q), 16, b_off[q & 1] + q * b_blk,
-                                               gen * 128, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void_t*)(sm.b[wave] + 1024 * q), 16, b_off[q & 1],
+                                               gen * 128 + q * b_blk, 0, 0);   // block q: a scalar offset
   };
   auto issue_s = [&](int chunk) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void_t*)(sm.s8[chunk & 1] + 1024 * wave), 16, s_off,
@@ -1116,6 +1116,215 @@ k_grouped_mm_fwd_w4a4(const uint8_t* __restrict__ xq, const uint8_t* __restrict_
                       ti.row_end, col0 + wn * 64, ndim);
 }
 
+// ------------------------------------------------------------- forward, W4A8
+// y[rows_e] = q8(x)[rows_e] @ W_e^T with the activations in fp8: E4M3 codes
+// [T, K] with one E8M0 scale per 32 k [T, K/32], as quantize_cache_packed(x,
+// "fp8", 32) stores them (the fp8 form of "nemo_automodel.components.models.
+// deepseek_v41.quantization" quantize_cache; "NVIDIA Model Optimizer: from
+// mtq.quantize to a 4.95-bit DeepSeek-R1", sections "NVFP4 in the code: two
+// scales and a nibble" and "The claims, marked reported", for activation
+// scales computed at run time and the W4A8 form).  Both operands go as
+// stored into gfx950's block-scaled MFMA v_mfma_scale_f32_32x32x64_f8f6f4,
+// weights (e2m1, 16 bytes per lane: column l % 32, the 32 k of block h =
+// l / 32 of the 64-k sub-step) first, activations (E4M3, 32 bytes per lane:
+// row l % 32, bytes 0-15 the 16 k of slice h and bytes 16-31 those of slice
+// h + 2, slices of 16 k) second, each lane's E8M0 block scale in byte 0 of
+// its scale operand.  This pairing of an 8-bit with a 4-bit operand was read
+// off the one-hot parity test: with 32 consecutive k per lane the products
+// of slices 1 and 2 were crossed.  Products of codes and power-of-two scales
+// are exact, sums run in fp32, the output rounds to bf16 nearest-even.
+//
+// Organised like the whole-line bf16 forward: 96 x 256 tiles of 4 waves, two
+// workgroups per CU, wave w owning columns [64 w, +64) of the tile (3 x 2
+// MFMA tiles computed transposed).  Every global transfer is a whole
+// 128-byte line:
+//  * activations: a stage is 128 bytes (128 k) of each of the tile's 96
+//    rows, two stages (12 KB each), 16-byte chunks swizzled by
+//    (row >> 1) & 7 as in the bf16 kernels;
+//  * weights: per wave, a generation of 64 columns x 128 bytes (256 k = two
+//    stages), copied into registers at its first stage, the area then
+//    refilled with the next generation;
+//  * scales: 16 bytes (512 k = four stages) per row and per column,
+//    double-buffered.
+// Each stage issues everything the next needs (scale chunks, the next weight
+// generation, then the next activation stage) and ends by waiting for all of
+// it (s_waitcnt vmcnt(0)) and the barrier: one stage of lead for every
+// transfer.  Needs K % 512 == 0.
+constexpr int kW8BM = 96, kW8BN = 256, kW8Threads = 256;
+
+struct W8Smem {
+  uint8_t a[2][kW8BM * 128];          // activation stages: 96 rows x 128 bytes (128 k of E4M3)
+  uint8_t b[4][64 * 128];             // weight generation per wave: 64 columns x 128 bytes (256 k)
+  uint8_t sa[2][128 * 16];            // activation scales: 16 bytes (512 k) per row (two 64-row transfers)
+  uint8_t sb[2][kW8BN * 16];          // weight scales: 16 bytes (512 k) per column
+};
+
+__global__ void __launch_bounds__(kW8Threads, 2)
+k_grouped_mm_fwd_w4a8(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+                      const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
+                      const int32_t* __restrict__ offs, int experts, int64_t tokens, int64_t ndim, int64_t kdim,
+                      uint8_t* __restrict__ out, int gx) {
+  constexpr int BM = kW8BM, BN = kW8BN, MT = BM / 32, NT = 2, QA = BM / 32, kThreads = kW8Threads;
+  const int64_t col0 = (int64_t)(blockIdx.x % gx) * BN;
+  TileTable<BM> tt;
+  tt.build(offs, experts, tokens);
+  const TileInfo ti = tt.lookup((int)(blockIdx.x / gx));
+  if (ti.expert == -2) return;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, r = lane & 31;
+
+  if (ti.expert == -1) {
+    for (int i = threadIdx.x; i < BM * BN / 8; i += kThreads) {
+      const int rr = i / (BN / 8), c = (i % (BN / 8)) * 8;
+      const int64_t gr = ti.row0 + rr, gc = col0 + c;
+      if (gr < ti.row_end && gc < ndim) {
+        unsigned short* dst = reinterpret_cast<unsigned short*>(out + (gr * ndim + gc) * 2);
+        for (int q = 0; q < 8 && gc + q < ndim; ++q) dst[q] = 0;
+      }
+    }
+    return;
+  }
+
+  __shared__ __attribute__((aligned(1024))) W8Smem sm;
+
+  const int64_t prow = kdim / 2, srow = kdim / 32;
+  const int64_t nrows = min(ti.row_end - ti.row0, (int64_t)BM);
+  // activations: wave w fills blocks QA w .. QA w + QA - 1 of 8 rows (lane l ->
+  // row 8b + l/8, LDS chunk l%8 <- global chunk (l%8) ^ ((row >> 1) & 7));
+  // ranges cover this tile's rows (reads past them return zeros)
+  const __amdgpu_buffer_rsrc_t rs_a = dma_rsrc(xq + ti.row0 * kdim, nrows * kdim);
+  uint32_t a_off[QA];
+#pragma unroll
+  for (int q = 0; q < QA; ++q) {
+    const int row = 8 * (QA * wave + q) + (lane >> 3);
+    a_off[q] = (uint32_t)(row * kdim + 16 * ((lane & 7) ^ ((row >> 1) & 7)));
+  }
+  // activation scales: waves 0 and 1 move rows 64 w + lane (16 bytes each)
+  const __amdgpu_buffer_rsrc_t rs_sa = dma_rsrc(xs + ti.row0 * srow, nrows * srow);
+  const uint32_t sa_off = (uint32_t)((64 * (wave & 1) + lane) * srow);
+  // weights: this wave's 64 columns, block q (0 .. 7) = columns 8q .. 8q+7,
+  // lane l -> column 8q + l/8, LDS chunk l%8 <- line chunk (l%8) ^ (column >> 1 & 7)
+  // (column 8q + c: ((8q + c) >> 1) & 7 = (c >> 1) ^ 4 (q & 1))
+  const int64_t n0 = col0 + 64 * wave;
+  const __amdgpu_buffer_rsrc_t rs_b =
+      dma_rsrc(packed_e_of(packed, ti.expert, ndim, kdim) + n0 * prow, (ndim - n0) * prow);
+  const int bc = lane >> 3;
+  const uint32_t b_off[2] = {(uint32_t)(bc * prow + 16 * ((lane & 7) ^ (bc >> 1))),
+                             (uint32_t)(bc * prow + 16 * ((lane & 7) ^ (bc >> 1) ^ 4))};
+  const uint32_t b_blk = (uint32_t)(8 * prow);
+  // weight scales of this wave's columns: lane l <- column 64 w + l
+  const __amdgpu_buffer_rsrc_t rs_sb = dma_rsrc(scales + ((int64_t)ti.expert * ndim + n0) * srow, (ndim - n0) * srow);
+  const uint32_t sb_off = (uint32_t)(lane * srow);
+
+  const int nst = (int)(kdim / 128);          // stages of 128 k; a multiple of 4 (K % 512 == 0)
+  const int ngen = nst / 2, nchunk = nst / 4;
+  auto issue_a = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < QA; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_void_t*)(sm.a[st & 1] + 1024 * (QA * wave + q)), 16,
+                                               a_off[q], st * 128, 0, 0);
+  };
+  auto issue_b = [&](int gen) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void_t*)(sm.b[wave] + 1024 * q), 16, b_off[q & 1],
+                                               gen * 128 + q * b_blk, 0, 0);   // block q: a scalar offset
+  };
+  auto issue_scales = [&](int chunk) {
+    if (wave < 2)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_sa, (lds_void_t*)(sm.sa[chunk & 1] + 1024 * wave), 16, sa_off,
+                                               16 * chunk, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_sb, (lds_void_t*)(sm.sb[chunk & 1] + 1024 * wave), 16, sb_off,
+                                             16 * chunk, 0, 0);
+  };
+
+  f32x16_t acc[MT][NT];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[i][j] = f32x16_t{};
+
+  issue_scales(0);
+  issue_b(0);
+  issue_a(0);
+  __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);   // vmcnt(0)
+  __syncthreads();
+
+  u32x4_t pw[NT][4];                          // the generation's weight codes: [column tile][sub-step]
+  uint32_t swb[NT][2];                        // the generation's 8 weight scale bytes per column tile
+  const int swz = (r >> 1) & 7;               // rows 32i + r share the chunk swizzle
+  // stage s; g = s % 2 (a literal after inlining): which half of the generation
+  auto step = [&](int s, int g) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (g == 0) {
+      // copy generation s / 2 and its scale bytes (landed by the last barrier)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int c = 32 * j + r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          pw[j][u] = *reinterpret_cast<const u32x4_t*>(sm.b[wave] + c * 128 + 16 * ((2 * u + h) ^ ((c >> 1) & 7)));
+        const u32x2_t v = *reinterpret_cast<const u32x2_t*>(sm.sb[(s >> 2) & 1] + 16 * (64 * wave + c) +
+                                                            8 * ((s >> 1) & 1));
+        swb[j][0] = v.x;
+        swb[j][1] = v.y;
+      }
+    }
+    // the activation scale bytes of this stage (4 blocks of 32 k)
+    uint32_t sxa[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+      sxa[i] = *reinterpret_cast<const uint32_t*>(sm.sa[(s >> 2) & 1] + 16 * (32 * i + r) + 4 * (s & 3));
+    // everything the next stage needs: scale chunk, weight generation, activations
+    if ((s & 3) == 0 && (s >> 2) + 1 < nchunk) issue_scales((s >> 2) + 1);
+    if (g == 0 && (s >> 1) + 1 < ngen) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the copy has read the area
+      issue_b((s >> 1) + 1);
+    }
+    if (s + 1 < nst) issue_a(s + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* la = sm.a[s & 1] + r * 128;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      v8i32_t fx[MT];
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
+        // 16-k slices h and h + 2 of the sub-step (16-byte chunks 4u + h, 4u + 2 + h)
+        const u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(la + i * 32 * 128 + 16 * ((4 * u + h) ^ swz));
+        const u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(la + i * 32 * 128 + 16 * ((4 * u + 2 + h) ^ swz));
+        fx[i] = v8i32_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+      }
+      const int wu = 2 * g + u;                 // sub-step within the weight generation
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const u32x4_t p = pw[j][wu];
+        const v8i32_t w = {(int)p.x, (int)p.y, (int)p.z, (int)p.w, 0, 0, 0, 0};
+        const uint32_t sw = (swb[j][(2 * wu + h) >> 2] >> (8 * ((2 * wu + h) & 3))) & 0xFFu;
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          const uint32_t sx = (sxa[i] >> (8 * (2 * u + h))) & 0xFFu;
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w, fx[i], acc[i][j], 4, 0, 0, (int)sw, 0,
+                                                                       (int)sx);
+        }
+      }
+    }
+    if (s + 1 < nst) {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);   // vmcnt(0): all the next stage needs has landed
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int s = 0; s < nst; s += 2) {
+    step(s, 0);
+    step(s + 1, 1);
+  }
+  __syncthreads();
+  static_assert(sizeof(W8Smem) >= (size_t)4 * BM * 128, "epilogue block fits");
+  store_block_lds<MT>(reinterpret_cast<uint8_t*>(&sm) + wave * BM * 128, acc, lane, out, ndim, ti.row0, ti.row_end,
+                      col0 + 64 * wave, ndim);
+}
+
 // ----------------------------------------------------------------- backward
 // grad_x = grad_out @ W_e.  Tile: 256 token rows x 256 output columns (k),
 // reduction over n in steps of 64; 8 waves, one workgroup per CU.  Wave
@@ -1446,6 +1655,17 @@ hipError_t launch_grouped_mm_w4a4(const void* xq, const uint8_t* xs, int64_t tok
   const int64_t gy = (tokens + kW4BM - 1) / kW4BM + experts;
   if (!grid_fits(gx * gy, kW4Threads)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(k_grouped_mm_fwd_w4a4, dim3((unsigned)(gx * gy)), dim3(kW4Threads), 0, st, (const uint8_t*)xq, xs,
+                     (const uint8_t*)packed, scales, offs, (int)experts, tokens, n, k, (uint8_t*)out, (int)gx);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_mm_w4a8(const void* xq, const uint8_t* xs, int64_t tokens, const int8_t* packed,
+                                  const uint8_t* scales, int64_t experts, int64_t n, int64_t k, const int32_t* offs,
+                                  void* out, hipStream_t st) {
+  const int64_t gx = (n + kW8BN - 1) / kW8BN;
+  const int64_t gy = (tokens + kW8BM - 1) / kW8BM + experts;
+  if (!grid_fits(gx * gy, kW8Threads)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(k_grouped_mm_fwd_w4a8, dim3((unsigned)(gx * gy)), dim3(kW8Threads), 0, st, (const uint8_t*)xq, xs,
                      (const uint8_t*)packed, scales, offs, (int)experts, tokens, n, k, (uint8_t*)out, (int)gx);
   return hipGetLastError();
 }

@@ -38,4 +38,9 @@ hipError_t launch_grouped_mm_w4a4(const void* xq, const uint8_t* xs, int64_t tok
                                   const uint8_t* scales, int64_t experts, int64_t n, int64_t k, const int32_t* offs,
                                   void* out, hipStream_t st);
 
+// out[T, N] = dq(xq)[T, K] dq(W_e)^T, activations E4M3 with E8M0 block-32 scales (K % 512 == 0).
+hipError_t launch_grouped_mm_w4a8(const void* xq, const uint8_t* xs, int64_t tokens, const int8_t* packed,
+                                  const uint8_t* scales, int64_t experts, int64_t n, int64_t k, const int32_t* offs,
+                                  void* out, hipStream_t st);
+
 }  // namespace mxq

@@ -12,7 +12,7 @@ Names and signatures follow the pages:
   ``quantize_cache`` and ``_CacheQuantization``.
 * "NVIDIA Model Optimizer: from mtq.quantize to a 4.95-bit DeepSeek-R1":
   ``quantize_nvfp4`` / ``dequantize_nvfp4`` (two-level NVFP4) and the W4A4
-  forward ``mxfp4_grouped_mm_fwd_w4a4``.
+  and W4A8 forwards ``mxfp4_grouped_mm_fwd_w4a4`` / ``mxfp4_grouped_mm_fwd_w4a8``.
 """
 
 import torch
@@ -349,6 +349,46 @@ def mxfp4_grouped_mm_fwd_w4a4(x, packed, scales, offs):
         raise TypeError("mxfp4_grouped_mm_fwd_w4a4: x must be bfloat16 [tokens, K]")
     xq, xs = quantize_mxfp4(x)
     return mxfp4_grouped_mm_fwd_w4a4_quantized(xq, xs, packed, scales, offs)
+
+
+def mxfp4_grouped_mm_fwd_w4a8_quantized(xq, xs, packed, scales, offs):
+    """y [T, N] = dq(xq)[rows_e] @ dq(W_e)^T per expert segment, activations
+    already in fp8 (uint8 E4M3 codes [T, K] and E8M0 scale bytes [T, K/32], as
+    ``quantize_cache_packed(x, "fp8", 32)`` returns them); K % 512 == 0.  bf16
+    output."""
+    _need_cuda(xq, xs, packed, scales, offs)
+    xs8, s = _as_u8(xs), _as_u8(scales)
+    if xq.dtype != torch.uint8:
+        raise TypeError("mxfp4_grouped_mm_fwd_w4a8: xq must be uint8 E4M3 codes")
+    if offs.dtype != torch.int32:
+        raise TypeError("mxfp4_grouped_mm_fwd_w4a8: offs must be int32")
+    if packed.dim() != 3 or s.dim() != 3 or offs.dim() != 1 or xq.dim() != 2 or xs8.dim() != 2:
+        raise ValueError("mxfp4_grouped_mm_fwd_w4a8: xq [T, K], xs [T, K/32], packed [E, N, K/2], "
+                         "scales [E, N, K/32], offs [E]")
+    E, N, K2 = packed.shape
+    T, K = xq.shape
+    if (K != 2 * K2 or tuple(s.shape) != (E, N, K // 32) or offs.shape[0] != E
+            or tuple(xs8.shape) != (T, K // 32)):
+        raise ValueError("mxfp4_grouped_mm_fwd_w4a8: inconsistent shapes")
+    xq, xs8, p, s, o = xq.contiguous(), xs8.contiguous(), packed.contiguous(), s.contiguous(), offs.contiguous()
+    y = torch.empty(T, N, dtype=torch.bfloat16, device=xq.device)
+    with torch.cuda.device(xq.device):
+        st = _lib.lib().mxfp4_grouped_mm_fwd_w4a8(_ptr(xq), _ptr(xs8), T, K, _ptr(p), _ptr(s), E, N, _ptr(o),
+                                                  _ptr(y), _stream(xq.device))
+    _lib.check(st, "mxfp4_grouped_mm_fwd_w4a8")
+    return y
+
+
+def mxfp4_grouped_mm_fwd_w4a8(x, packed, scales, offs):
+    """W4A8 forward: the activations quantized to fp8 (E4M3 codes, one E8M0
+    power-of-two scale per 32 columns: ``quantize_cache_packed(x, "fp8",
+    32)``), then the grouped GEMM of fp8 activations and MXFP4 weights on the
+    block-scaled MFMA.  bf16 x [T, K], K % 512 == 0."""
+    _need_cuda(x)
+    if x.dtype != torch.bfloat16 or x.dim() != 2:
+        raise TypeError("mxfp4_grouped_mm_fwd_w4a8: x must be bfloat16 [tokens, K]")
+    xq, xs = quantize_cache_packed(x, "fp8", 32)
+    return mxfp4_grouped_mm_fwd_w4a8_quantized(xq, xs, packed, scales, offs)
 
 
 class MXFP4GroupedMM(torch.autograd.Function):

@@ -44,4 +44,9 @@ hipError_t launch_grouped_mm_w4a4(const void*, const uint8_t*, int64_t, const in
   return reached();
 }
 
+hipError_t launch_grouped_mm_w4a8(const void*, const uint8_t*, int64_t, const int8_t*, const uint8_t*, int64_t, int64_t,
+                                  int64_t, const int32_t*, void*, hipStream_t) {
+  return reached();
+}
+
 }  // namespace mxq

@@ -188,3 +188,30 @@ def test_nvfp4_mse_validation(L):
     assert q(FAKE, 1, 4, 32, FAKE * 2, FAKE * 2 + 8, FAKE * 4, None) == -7   # scales inside packed
     assert q(FAKE, 1, 4, 0, FAKE * 2, FAKE * 3, FAKE * 4, None) == 0
 
+
+
+def test_grouped_mm_w4a8_validation(L):
+    f = L.mxfp4_grouped_mm_fwd_w4a8
+    # (xq, xs, tokens, k, packed, scales, experts, n, offs, y, stream)
+    ok = (FAKE, FAKE * 2, 16, 512, FAKE * 3, FAKE * 4, 2, 64, FAKE * 5, FAKE * 6, None)
+    names = ("xq", "xs", "tokens", "k", "packed", "scales", "experts", "n", "offs", "y", "stream")
+
+    def call(**kw):
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return f(*[args[n] for n in names])
+    assert call(k=256) == -2                      # whole 512-k scale chunks
+    assert call(k=544) == -2
+    assert call(n=60) == -2                       # n % 8
+    assert call(experts=-1) == -2
+    assert call(k=1 << 22) == -2                  # 32-bit offsets
+    assert call(k=1 << 16, n=1 << 16) == -2       # one expert's packed weights reach 2 GiB
+    assert call(xq=None) == -1
+    assert call(offs=None) == -1
+    assert call(xq=FAKE + 4) == -6                # every operand 16-byte aligned
+    assert call(packed=FAKE * 3 + 8) == -6
+    assert call(y=FAKE * 6 + 2) == -6
+    assert call(y=FAKE + 4096) == -7              # y overlaps xq (16 rows x 512 bytes)
+    assert call(y=FAKE * 2 + 16) == -7            # y overlaps xs
+    assert call(tokens=0) == 0                    # nothing to do
+    assert call(n=0) == 0
