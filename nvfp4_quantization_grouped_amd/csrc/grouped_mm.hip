@@ -475,6 +475,10 @@ struct DmaSrc {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t dma_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(bytes > 0 ? bytes : 0), 0x00020000);
 }
+// a lane offset past every range used here (the lane reads zeros); the range
+// check covers the lane offset, so a transfer whose scalar offset moves it
+// to other rows takes this offset for blocks past the valid rows
+constexpr uint32_t kBufOob = 0x80000000u;
 
 // Op q of one step's transfers of one wave, straight into LDS (q < QA:
 // activation block q; then the 2 weight blocks; then, with SCH == 2, the
@@ -773,7 +777,8 @@ __device__ __forceinline__ void fwd_fl_body(const uint8_t* __restrict__ a, const
   auto issue_b = [&](int gen) {
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void_t*)(sm.b[wave] + 1024 * q), 16, b_off[q & 1],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void_t*)(sm.b[wave] + 1024 * q), 16,
+                                               n0 + 8 * q < ndim ? b_off[q & 1] : kBufOob,
                                                gen * 128 + q * b_blk, 0, 0);   // block q: a scalar offset
   };
   auto issue_s = [&](int chunk) {
@@ -1227,7 +1232,8 @@ k_grouped_mm_fwd_w4a8(const uint8_t* __restrict__ xq, const uint8_t* __restrict_
   auto issue_b = [&](int gen) {
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void_t*)(sm.b[wave] + 1024 * q), 16, b_off[q & 1],
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void_t*)(sm.b[wave] + 1024 * q), 16,
+                                               n0 + 8 * q < ndim ? b_off[q & 1] : kBufOob,
                                                gen * 128 + q * b_blk, 0, 0);   // block q: a scalar offset
   };
   auto issue_scales = [&](int chunk) {
@@ -1370,7 +1376,6 @@ __device__ __forceinline__ int wd_swz(int n) { return (((n >> 1) & 1) << 2) | ((
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-constexpr uint32_t kBufOob = 0x80000000u;   // offset past every range used here
 
 struct WRaw {          // one step's weight piece of a lane (16 packed bytes + scale byte)
   u32x4_t pk;
