@@ -43,6 +43,8 @@ MFMA_FP4_PEAK_TFLOPS = 10100.0   # MI355X dense fp4 (MXFP4) MFMA
 MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 # fp32 VALU issue rate without packed (two-wide) fp32 or FMA pairing: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
 ALU_FP32_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
+# MI355X's published fp32 vector peak (packed two-wide FMAs, two flops each): 4x the issue rate above
+FP32_PUBLISHED_TFLOPS = 157.3
 METRIC = "quant/dequant GB/s (% HBM peak); MXFP4 grouped-GEMM TFLOP/s (% MFMA peak)"
 
 
@@ -356,7 +358,8 @@ def main():
             d.update({"GB": round(leg.work / 1e9, 4), "GB/s": round(rate, 1), "frac_hbm": round(rate / HBM_PEAK_GBPS, 4)})
         if leg.alu_ops:
             tops = leg.alu_ops / (per_call_ms * 1e-3) / 1e12
-            d.update({"bound": "alu", "Tops/s": round(tops, 2), "frac_alu": round(tops / ALU_FP32_PEAK_TOPS, 4)})
+            d.update({"bound": "alu", "Tops/s": round(tops, 2), "frac_alu": round(tops / ALU_FP32_PEAK_TOPS, 4),
+                      "frac_fp32_published": round(tops / FP32_PUBLISHED_TFLOPS, 4)})
         out_legs.append(d)
 
     moe_legs = [l for l in legs if l.name.startswith("moe.")]

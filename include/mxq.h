@@ -43,7 +43,8 @@ typedef enum {
   MXQ_ERR_BLOCK = -5,   /* block_size <= 0 (or odd for packed fp4 storage)     */
   MXQ_ERR_ALIGN = -6,   /* grouped GEMM activation / packed weights / output not 16-B aligned */
   MXQ_ERR_ALIAS = -7,   /* output overlaps an input that must stay unmodified  */
-  MXQ_ERR_HIP = -8      /* a HIP launch reported an error                      */
+  MXQ_ERR_HIP = -8,     /* a HIP launch reported an error                      */
+  MXQ_ERR_OFFS = -9     /* mxq_validate_offs: offs breaks its precondition     */
 } mxq_status;
 
 typedef enum { MXQ_F32 = 0, MXQ_BF16 = 1, MXQ_F16 = 2 } mxq_dtype;
@@ -222,6 +223,24 @@ int mxfp4_grouped_mm_fwd(const void* x, int64_t tokens, int64_t k,
 int mxfp4_grouped_mm_bwd_x(const void* grad_out, int64_t tokens, int64_t n,
                            const int8_t* packed, const uint8_t* scales, int64_t experts, int64_t k,
                            const int32_t* offs, void* grad_x, void* stream);
+
+/*
+ * mxq_validate_offs -- debug check of the offs precondition of the grouped
+ * GEMM entry points ([MX] MXFP4GroupedMM: offs holds the cumulative token
+ * counts of the experts, so it is non-decreasing and ends within the
+ * tokens).  The GEMMs do not check offs on the host (that would need a device
+ * sync) and clamp it instead; this entry point is for callers who want the
+ * violation reported.  It copies offs int32 [experts] (DEVICE) to host memory
+ * on `stream` and WAITS for the stream -- the one entry point that
+ * synchronizes -- then checks 0 <= offs[0] <= offs[1] <= ... <=
+ * offs[experts-1] <= tokens.  *first_bad (may be NULL) receives the first
+ * expert index whose offset breaks it, else -1.
+ * Returns MXQ_OK, MXQ_ERR_OFFS (violated), MXQ_ERR_NULL (offs NULL with
+ * experts > 0), MXQ_ERR_SHAPE (experts or tokens negative, or experts >
+ * 2^26), MXQ_ERR_HIP (the copy or the wait failed).  experts == 0 is MXQ_OK
+ * without any HIP call.
+ */
+int mxq_validate_offs(const int32_t* offs, int64_t experts, int64_t tokens, int64_t* first_bad, void* stream);
 
 /*
  * mxfp4_grouped_mm_fwd_w4a4 -- the forward with the activations in MXFP4 too

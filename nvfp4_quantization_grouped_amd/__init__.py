@@ -27,6 +27,7 @@ from .ops import (
     quantize_mxfp4,
     quantize_nvfp4,
     quantize_nvfp4_mse,
+    validate_offs,
 )
 
 __all__ = [
@@ -37,5 +38,5 @@ __all__ = [
     "mxfp4_grouped_mm_fwd_w4a8", "mxfp4_grouped_mm_fwd_w4a8_quantized",
     "quantize_cache", "quantize_cache_bwd", "quantize_cache_forward", "quantize_mxfp4",
     "quantize_nvfp4", "dequantize_nvfp4", "quantize_cache_packed", "dequantize_cache_packed",
-    "quantize_nvfp4_mse",
+    "quantize_nvfp4_mse", "validate_offs",
 ]

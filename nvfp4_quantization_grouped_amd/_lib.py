@@ -14,12 +14,13 @@ LIB_PATH = os.path.join(_HERE, "libmxq.so")
 # mxq_dtype / mxq_format codes (include/mxq.h)
 MXQ_F32, MXQ_BF16, MXQ_F16 = 0, 1, 2
 MXQ_FMT_FP8, MXQ_FMT_MXFP4, MXQ_FMT_NVFP4 = 0, 1, 2
+MXQ_ERR_OFFS = -9
 
 EXPORTS = (
     "quantize_mxfp4", "dequantize_mxfp4", "quantize_cache", "quantize_cache_bwd", "quantize_nvfp4", "dequantize_nvfp4",
     "quantize_cache_packed", "dequantize_cache_packed", "quantize_nvfp4_mse",
     "mxfp4_grouped_mm_fwd", "mxfp4_grouped_mm_bwd_x", "mxfp4_grouped_mm_fwd_w4a4", "mxfp4_grouped_mm_fwd_w4a8",
-    "mxq_status_string",
+    "mxq_validate_offs", "mxq_status_string",
 )
 
 _lib = None
@@ -39,6 +40,7 @@ _SIGS = {
     "mxfp4_grouped_mm_bwd_x": ([_vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp], _int),
     "mxfp4_grouped_mm_fwd_w4a4": ([_vp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp], _int),
     "mxfp4_grouped_mm_fwd_w4a8": ([_vp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp], _int),
+    "mxq_validate_offs": ([_vp, _i64, _i64, _vp, _vp], _int),
     "mxq_status_string": ([_int], ctypes.c_char_p),
 }
 

@@ -1,5 +1,6 @@
 // C ABI of libmxq (declared in include/mxq.h): host-side validation, then
 // one asynchronous launch on the caller's stream.  No allocation, no sync.
+#include <vector>
 #include "../../include/mxq.h"
 #include "launch.hpp"
 
@@ -193,6 +194,24 @@ int mxfp4_grouped_mm_bwd_x(const void* grad_out, int64_t tokens, int64_t n, cons
       mxq::launch_grouped_mm(true, grad_out, tokens, packed, scales, experts, n, k, offs, grad_x, (hipStream_t)stream));
 }
 
+int mxq_validate_offs(const int32_t* offs, int64_t experts, int64_t tokens, int64_t* first_bad, void* stream) {
+  if (first_bad) *first_bad = -1;
+  if (experts < 0 || tokens < 0 || experts > (int64_t(1) << 26)) return MXQ_ERR_SHAPE;
+  if (experts == 0) return MXQ_OK;
+  if (!offs) return MXQ_ERR_NULL;
+  std::vector<int32_t> h((size_t)experts);
+  if (mxq::copy_to_host_sync(offs, h.data(), experts * 4, (hipStream_t)stream) != hipSuccess) return MXQ_ERR_HIP;
+  int64_t prev = 0;
+  for (int64_t e = 0; e < experts; ++e) {
+    if (h[(size_t)e] < prev || h[(size_t)e] > tokens) {
+      if (first_bad) *first_bad = e;
+      return MXQ_ERR_OFFS;
+    }
+    prev = h[(size_t)e];
+  }
+  return MXQ_OK;
+}
+
 int mxfp4_grouped_mm_fwd_w4a4(const int8_t* xq, const uint8_t* xs, int64_t tokens, int64_t k, const int8_t* packed,
                               const uint8_t* scales, int64_t experts, int64_t n, const int32_t* offs, void* y,
                               void* stream) {
@@ -242,6 +261,7 @@ const char* mxq_status_string(int s) {
     case MXQ_ERR_ALIGN: return "misaligned pointer (grouped GEMM activations, packed weights and output need 16-byte alignment)";
     case MXQ_ERR_ALIAS: return "output overlaps an input";
     case MXQ_ERR_HIP: return "HIP launch error";
+    case MXQ_ERR_OFFS: return "offs is not non-decreasing within [0, tokens]";
     default: return "unknown status";
   }
 }

@@ -29,6 +29,8 @@ hipError_t launch_dequantize_cache_packed(const uint8_t* codes, const uint8_t* s
                                           int fmt, int32_t block, void* out, int dt, hipStream_t st);
 hipError_t launch_copy(const void* src, void* dst, int64_t bytes, hipStream_t st);
 hipError_t launch_zero(void* dst, int64_t bytes, hipStream_t st);
+// device -> host copy on st, then wait for st (used only by the offs debug check)
+hipError_t copy_to_host_sync(const void* src, void* dst, int64_t bytes, hipStream_t st);
 // bwd = false: out[T, N] = a[T, K] W_e^T;  bwd = true: out[T, K] = a[T, N] W_e.
 hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8_t* packed, const uint8_t* scales,
                              int64_t experts, int64_t wn_dim, int64_t wk_dim, const int32_t* offs, void* out,

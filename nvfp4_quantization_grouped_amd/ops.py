@@ -15,6 +15,8 @@ Names and signatures follow the pages:
   and W4A8 forwards ``mxfp4_grouped_mm_fwd_w4a4`` / ``mxfp4_grouped_mm_fwd_w4a8``.
 """
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -285,6 +287,23 @@ def _gemm_args(a, packed, scales, offs):
     if tuple(s.shape) != (E, N, K2 * 2 // 32) or offs.shape[0] != E:
         raise ValueError("MXFP4GroupedMM: inconsistent packed / scales / offs shapes")
     return a.contiguous(), packed.contiguous(), s.contiguous(), offs.contiguous(), E, N, K2 * 2
+
+
+def validate_offs(offs, tokens):
+    """Debug check of the grouped GEMM's offs precondition (non-decreasing,
+    within [0, tokens]); synchronizes the current stream.  Returns -1 when it
+    holds, else the first expert index that breaks it."""
+    _need_cuda(offs)
+    if offs.dtype != torch.int32 or offs.dim() != 1:
+        raise TypeError("validate_offs: offs must be a 1-D int32 tensor")
+    o = offs.contiguous()
+    bad = ctypes.c_int64(-1)
+    with torch.cuda.device(o.device):
+        st = _lib.lib().mxq_validate_offs(_ptr(o), o.shape[0], int(tokens), ctypes.byref(bad), _stream(o.device))
+    if st == _lib.MXQ_ERR_OFFS:
+        return int(bad.value)
+    _lib.check(st, "mxq_validate_offs")
+    return -1
 
 
 def mxfp4_grouped_mm_fwd(x, packed, scales, offs):

@@ -35,6 +35,7 @@ hipError_t launch_dequantize_cache_packed(const uint8_t*, const uint8_t*, int64_
 }
 hipError_t launch_copy(const void*, void*, int64_t, hipStream_t) { return reached(); }
 hipError_t launch_zero(void*, int64_t, hipStream_t) { return reached(); }
+hipError_t copy_to_host_sync(const void*, void*, int64_t, hipStream_t) { return reached(); }
 hipError_t launch_grouped_mm(bool, const void*, int64_t, const int8_t*, const uint8_t*, int64_t, int64_t, int64_t,
                              const int32_t*, void*, hipStream_t) {
   return reached();

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(L):
 
 
 def test_status_strings(L):
-    for s in range(0, -9, -1):
+    for s in range(0, -10, -1):
         msg = L.mxq_status_string(s)
         assert msg and msg != b"unknown status"
     assert L.mxq_status_string(12345) == b"unknown status"
@@ -215,3 +215,17 @@ def test_grouped_mm_w4a8_validation(L):
     assert call(y=FAKE * 2 + 16) == -7            # y overlaps xs
     assert call(tokens=0) == 0                    # nothing to do
     assert call(n=0) == 0
+
+
+def test_validate_offs_validation(L):
+    """mxq_validate_offs answers bad arguments and the empty case on the host
+    (the check itself copies offs from the device: GPU test)."""
+    bad = ctypes.c_int64(7)
+    f = L.mxq_validate_offs
+    assert f(FAKE, -1, 16, ctypes.byref(bad), None) == -2 and bad.value == -1
+    assert f(FAKE, 4, -1, ctypes.byref(bad), None) == -2
+    assert f(FAKE, (1 << 26) + 1, 16, ctypes.byref(bad), None) == -2
+    assert f(None, 4, 16, ctypes.byref(bad), None) == -1
+    bad.value = 7
+    assert f(None, 0, 16, ctypes.byref(bad), None) == 0 and bad.value == -1   # no experts: holds, no HIP call
+    assert f(None, 0, 16, None, None) == 0                                      # first_bad may be NULL

@@ -302,3 +302,21 @@ def test_many_experts(E, clamp):
     check_segments(bf16_values(gx), want_b, offs, what=f"E={E} bwd_x")
     y4 = mxq.mxfp4_grouped_mm_fwd_w4a4(to_gpu_bits(xb, "bf16"), pt, st, ot)
     check_segments(bf16_values(y4), oracle.grouped_mm_fwd_w4a4(x, packed, scales, offs), offs, what=f"E={E} w4a4")
+
+
+@pytest.mark.gpu
+def test_validate_offs():
+    """The offs debug check: valid offsets (empty experts included) hold;
+    a decrease, a negative first offset and an end past the tokens are
+    reported at the first expert that breaks the precondition."""
+    def check(raw, tokens):
+        return mxq.validate_offs(torch.tensor(raw, dtype=torch.int32, device=dev()), tokens)
+    assert check([0, 10, 10, 40], 40) == -1
+    assert check([0, 0, 0], 0) == -1
+    assert check([5, 9, 40], 64) == -1
+    assert check([5, 4, 40], 64) == 1
+    assert check([-1, 4, 40], 64) == 0
+    assert check([5, 9, 65], 64) == 2
+    assert check([5, 70, 60], 64) == 1
+    assert check(list(range(0, 4000, 2)), 3998) == -1          # many experts
+    assert check(list(range(0, 4000, 2)), 3996) == 1999
