@@ -159,11 +159,11 @@ def main():
             legs += [
                 Leg("w4a4.gate_up.quantize_x", "k_quantize_mxfp4<bf16>", "byte", T * H * (2 + 0.5 + 1 / 32),
                     quant(x_routed, H, gu_xq, gu_xs)),
-                Leg("w4a4.gate_up.fwd", "k_grouped_mm_fwd_w4a4", "flop", 2.0 * moe_rows * I2 * H,
+                Leg("w4a4.gate_up.fwd", "k_grouped_mm_fwd_w4a4_128", "flop", 2.0 * moe_rows * I2 * H,
                     w4(gu_xq, gu_xs, gu_p, gu_s, I2, H, gu_y), peak=MFMA_FP4_PEAK_TFLOPS),
                 Leg("w4a4.down.quantize_x", "k_quantize_mxfp4<bf16>", "byte", T * I * (2 + 0.5 + 1 / 32),
                     quant(h, I, dn_xq, dn_xs)),
-                Leg("w4a4.down.fwd", "k_grouped_mm_fwd_w4a4", "flop", 2.0 * moe_rows * H * I,
+                Leg("w4a4.down.fwd", "k_grouped_mm_fwd_w4a4_128", "flop", 2.0 * moe_rows * H * I,
                     w4(dn_xq, dn_xs, dn_p, dn_s, H, I, dn_y), peak=MFMA_FP4_PEAK_TFLOPS),
             ]
 

@@ -917,47 +917,64 @@ k_grouped_mm_fwd_fl96(const uint8_t* __restrict__ a, const uint8_t* __restrict__
 // e2m1 codes and two power-of-two scales are exact, sums run in fp32, the
 // output rounds to bf16 nearest-even.
 //
-// Workgroup: 8 waves, a 256 x 256 output tile; wave (wm, wn) = (wave / 4,
-// wave % 4) owns rows [128 wm, +128) and columns [64 wn, +64), 4 x 2 MFMA
-// tiles computed transposed (weight fragment first, as in the bf16 kernels,
-// so the LDS-staged epilogue is shared).  The reduction runs in stages of
-// 128 k (64 bytes of each row), 2 MFMA sub-steps each, through a ring of 4
-// LDS stages filled by buffer->LDS DMA three stages ahead; a stage row's four
-// 16-byte chunks are XOR-swizzled by (row >> 2) & 3, so the 16 rows one
-// fragment read touches per LDS cycle hit 16 distinct bank groups.  Scales
-// come 16 bytes (512 k, 4 stages) per row at a time into a double buffer.
-// Needs K % 512 == 0 (16-byte aligned scale rows).
-constexpr int kW4BM = 256, kW4BN = 256, kW4Threads = 512, kW4Stages = 4;
+// Workgroup: BM x 256 tiles (BM = 128 or 96) of 4 waves, two workgroups per
+// CU, wave w owning columns [64 w, +64) of the tile (BM/32 x 2 MFMA tiles
+// computed transposed, weight fragment first, so the LDS-staged epilogue is
+// the bf16 kernels').  Organised like the W4A8 forward, with every global
+// transfer a whole 128-byte line; for fp4 a line of a row is 256 k, so:
+//  * activations: a stage is 128 bytes (256 k) of each of the tile's rows,
+//    two stages, 16-byte chunks swizzled by (row >> 1) & 7 as in the bf16
+//    kernels (conflict-free 16-lane fragment reads);
+//  * weights: per wave, a generation of 64 columns x 128 bytes (the same
+//    256 k), copied into registers at the start of its stage, the area then
+//    refilled with the next stage's generation;
+//  * scales: 16 bytes (512 k = two stages) per row and per column,
+//    double-buffered; a lane reads the 8 bytes of its stage once and the
+//    MFMA's scale byte select picks each sub-step's block (dwords shifted
+//    right by 8h, so the block of sub-step u sits in byte 2(u & 1) of dword
+//    u / 2).
+// A stage is 4 MFMA sub-steps of 64 k: per wave and stage the same bytes of
+// LDS traffic per MFMA cycle as the W4A8 kernel's 128-k stage (24 fp4 MFMAs
+// of 32 cycles against 12 fp8 x fp4 MFMAs of 64).  Each stage issues
+// everything the next needs (scale chunk, weight generation, activation
+// stage) and ends by waiting for it (vmcnt(0)) and the barrier.  Needs
+// K % 512 == 0.
+constexpr int kW4BN = 256, kW4Threads = 256;
 
+template <int BM>
 struct W4Smem {
-  uint8_t a[kW4Stages][kW4BM * 64];   // activation codes: 256 rows x 64 bytes (128 k) per stage
-  uint8_t b[kW4Stages][kW4BN * 64];   // weight codes: 256 columns x 64 bytes
-  uint8_t sa[2][kW4BM * 16];          // activation scales: 16 bytes (512 k) per row
-  uint8_t sb[2][kW4BN * 16];          // weight scales
+  uint8_t a[2][BM * 128];             // activation stages: BM rows x 128 bytes (256 k of e2m1)
+  uint8_t b[4][64 * 128];             // weight generation per wave: 64 columns x 128 bytes (256 k)
+  uint8_t sa[2][128 * 16];            // activation scales: 16 bytes (512 k) per row (two 64-row transfers)
+  uint8_t sb[2][kW4BN * 16];          // weight scales: 16 bytes (512 k) per column
 };
 
 typedef int v8i32_t __attribute__((ext_vector_type(8)));
 
+// fp4 x fp4 block-scaled MFMA; SEL picks the scale byte of both scale operands
+template <int SEL>
 __device__ __forceinline__ f32x16_t mfma_w4(const u32x4_t& w, const u32x4_t& x, uint32_t sw, uint32_t sx,
                                             const f32x16_t& c) {
   const v8i32_t a = {(int)w.x, (int)w.y, (int)w.z, (int)w.w, 0, 0, 0, 0};
   const v8i32_t b = {(int)x.x, (int)x.y, (int)x.z, (int)x.w, 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, 0, (int)sw, 0, (int)sx);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 4, 4, SEL, (int)sw, SEL, (int)sx);
 }
 
-__global__ void __launch_bounds__(kW4Threads, 1)
-k_grouped_mm_fwd_w4a4(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
-                      const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
-                      const int32_t* __restrict__ offs, int experts, int64_t tokens, int64_t ndim, int64_t kdim,
-                      uint8_t* __restrict__ out, int gx) {
-  constexpr int BM = kW4BM, BN = kW4BN, MT = 4, NT = 2, S = kW4Stages, kThreads = kW4Threads;
+// (a device function template called by one kernel per tile height: clang
+// emitted no host launch stub for it as a kernel template)
+template <int BM>
+__device__ __forceinline__ void w4a4_body(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+                                          const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
+                                          const int32_t* __restrict__ offs, int experts, int64_t tokens, int64_t ndim,
+                                          int64_t kdim, uint8_t* __restrict__ out, int gx) {
+  constexpr int BN = kW4BN, MT = BM / 32, NT = 2, QA = BM / 32, kThreads = kW4Threads;
   const int64_t col0 = (int64_t)(blockIdx.x % gx) * BN;
   TileTable<BM> tt;
   tt.build(offs, experts, tokens);
   const TileInfo ti = tt.lookup((int)(blockIdx.x / gx));
   if (ti.expert == -2) return;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave >> 2, wn = wave & 3, h = lane >> 5, r = lane & 31;
+  const int h = lane >> 5, r = lane & 31;
 
   if (ti.expert == -1) {
     for (int i = threadIdx.x; i < BM * BN / 8; i += kThreads) {
@@ -971,40 +988,61 @@ k_grouped_mm_fwd_w4a4(const uint8_t* __restrict__ xq, const uint8_t* __restrict_
     return;
   }
 
-  __shared__ __attribute__((aligned(1024))) W4Smem sm;
+  __shared__ __attribute__((aligned(1024))) W4Smem<BM> sm;
 
-  // buffers over this tile's activation rows and weight columns (reads past
-  // the expert's rows or past n return zeros); ranges fit 31 bits (the
-  // launcher checks one expert's packed weights, and K < 2^22)
+  // buffers over this tile's rows and this wave's weight columns (reads past
+  // them return zeros); ranges fit 31 bits (the launcher checks one expert's
+  // packed weights, and K < 2^22)
   const int64_t prow = kdim / 2, srow = kdim / 32;
   const int64_t nrows = min(ti.row_end - ti.row0, (int64_t)BM);
+  // activations: wave w fills blocks QA w .. QA w + QA - 1 of 8 rows (lane l ->
+  // row 8b + l/8, LDS chunk l%8 <- line chunk (l%8) ^ ((row >> 1) & 7))
   const __amdgpu_buffer_rsrc_t rs_a = dma_rsrc(xq + ti.row0 * prow, nrows * prow);
-  const __amdgpu_buffer_rsrc_t rs_sa = dma_rsrc(xs + ti.row0 * srow, nrows * srow);
-  const __amdgpu_buffer_rsrc_t rs_b = dma_rsrc(packed_e_of(packed, ti.expert, ndim, kdim) + col0 * prow, (ndim - col0) * prow);
-  const __amdgpu_buffer_rsrc_t rs_sb =
-      dma_rsrc(scales + ((int64_t)ti.expert * ndim + col0) * srow, (ndim - col0) * srow);
-  // code transfers: op q (16 rows) of a stage, wave w moves ops 2w and 2w+1
-  // of both operands; lane l -> row 16q + l/4, LDS chunk l%4 <- global chunk
-  // (l%4) ^ ((row >> 2) & 3)
-  uint32_t c_off[2];
+  uint32_t a_off[QA];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 16 * (2 * wave + j) + (lane >> 2);
-    c_off[j] = (uint32_t)(row * prow + 16 * ((lane & 3) ^ ((row >> 2) & 3)));
+  for (int q = 0; q < QA; ++q) {
+    const int row = 8 * (QA * wave + q) + (lane >> 3);
+    a_off[q] = (uint32_t)(row * prow + 16 * ((lane & 7) ^ ((row >> 1) & 7)));
   }
-  // scale transfers: wave w < 4 moves activation rows 64w .. 64w+63, wave
-  // w >= 4 weight columns 64(w-4) ..; 16 bytes per lane
-  const bool s_is_a = wave < 4;
-  const uint32_t s_off = (uint32_t)((64 * (wave & 3) + lane) * srow);
-  auto issue_codes = [&](int st, int stage, int j) {   // j = 0, 1: the wave's two ops of one operand pair
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_void_t*)(sm.a[st] + 1024 * (2 * wave + j)), 16, c_off[j],
-                                             stage * 64, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void_t*)(sm.b[st] + 1024 * (2 * wave + j)), 16, c_off[j],
-                                             stage * 64, 0, 0);
+  // activation scales: waves 0 and 1 move rows 64 w + lane (16 bytes each)
+  const __amdgpu_buffer_rsrc_t rs_sa = dma_rsrc(xs + ti.row0 * srow, nrows * srow);
+  const uint32_t sa_off = (uint32_t)((64 * (wave & 1) + lane) * srow);
+  // weights: this wave's 64 columns, block q (0 .. 7) = columns 8q .. 8q+7,
+  // lane l -> column 8q + l/8, LDS chunk l%8 <- line chunk (l%8) ^ (column >> 1 & 7)
+  // (column 8q + c: ((8q + c) >> 1) & 7 = (c >> 1) ^ 4 (q & 1)); blocks past
+  // n take an out-of-range lane offset (the block offset is a scalar offset)
+  const int64_t n0 = col0 + 64 * wave;
+  const __amdgpu_buffer_rsrc_t rs_b =
+      dma_rsrc(packed_e_of(packed, ti.expert, ndim, kdim) + n0 * prow, (ndim - n0) * prow);
+  const int bc = lane >> 3;
+  const uint32_t b_off[2] = {(uint32_t)(bc * prow + 16 * ((lane & 7) ^ (bc >> 1))),
+                             (uint32_t)(bc * prow + 16 * ((lane & 7) ^ (bc >> 1) ^ 4))};
+  const uint32_t b_blk = (uint32_t)(8 * prow);
+  // weight scales of this wave's columns: lane l <- column 64 w + l
+  const __amdgpu_buffer_rsrc_t rs_sb = dma_rsrc(scales + ((int64_t)ti.expert * ndim + n0) * srow, (ndim - n0) * srow);
+  const uint32_t sb_off = (uint32_t)(lane * srow);
+
+  const int nst = (int)(kdim / 256);          // stages of 256 k; even (K % 512 == 0)
+  const int nchunk = nst / 2;
+  auto issue_a = [&](int st) {
+#pragma unroll
+    for (int q = 0; q < QA; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_void_t*)(sm.a[st & 1] + 1024 * (QA * wave + q)), 16,
+                                               a_off[q], st * 128, 0, 0);
+  };
+  auto issue_b = [&](int gen) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_b, (lds_void_t*)(sm.b[wave] + 1024 * q), 16,
+                                               n0 + 8 * q < ndim ? b_off[q & 1] : kBufOob,
+                                               gen * 128 + q * b_blk, 0, 0);
   };
   auto issue_scales = [&](int chunk) {
-    uint8_t* dst = (s_is_a ? sm.sa[chunk & 1] : sm.sb[chunk & 1]) + 1024 * (wave & 3);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(s_is_a ? rs_sa : rs_sb, (lds_void_t*)dst, 16, s_off, 16 * chunk, 0, 0);
+    if (wave < 2)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_sa, (lds_void_t*)(sm.sa[chunk & 1] + 1024 * wave), 16, sa_off,
+                                               16 * chunk, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_sb, (lds_void_t*)(sm.sb[chunk & 1] + 1024 * wave), 16, sb_off,
+                                             16 * chunk, 0, 0);
   };
 
   f32x16_t acc[MT][NT];
@@ -1013,112 +1051,97 @@ k_grouped_mm_fwd_w4a4(const uint8_t* __restrict__ xq, const uint8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[i][j] = f32x16_t{};
 
-  const int last = (int)(kdim / 128) - 1, last_chunk = last >> 2;
   issue_scales(0);
-#pragma unroll
-  for (int t = 0; t < S - 1; ++t) {
-    issue_codes(t, t, 0);
-    issue_codes(t, t, 1);
-  }
-  // stage 0 and scale chunk 0 have landed once only stages 1, 2 (4 ops each) may be in flight
-  wait_vmcnt_barrier<8>();
+  issue_b(0);
+  issue_a(0);
+  __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);   // vmcnt(0)
+  __syncthreads();
 
-  // fragment addresses: rows 128 wm + 32 i + r share (row >> 2) & 3 = (r >> 2) & 3
-  const int swz = (r >> 2) & 3;
-  const int a_row = (128 * wm + r) * 64, b_row = (64 * wn + r) * 64;
-  const int sa_row = (128 * wm + r) * 16, sb_row = (64 * wn + r) * 16;
-  struct Half {                  // one sub-step's fragments
-    u32x4_t x[MT], w[NT];
-  };
-  struct Scl {                   // a stage's scale dwords: blocks of (sub-step 0, half 0), (0, 1), (1, 0), (1, 1)
-    uint32_t x[MT], w[NT];
-  };
-  auto read_half = [&](Half& f, int s, int kk) {
-    const int st = s & (S - 1), off = 16 * ((2 * kk + h) ^ swz);
+  const int swz = (r >> 1) & 7;               // rows 32i + r share the chunk swizzle
+  const uint32_t sh = 8u * (uint32_t)h;
+  auto stage = [&](int s) {
+    __builtin_amdgcn_sched_barrier(0);
+    // this stage's weight generation and the 8 scale bytes (256 k) of every
+    // column and row tile, landed by the last barrier
+    u32x4_t pw[NT][4];
+    uint32_t swb[NT][2], sxa[MT][2];
+    const int sc_off = 8 * (s & 1);
 #pragma unroll
-    for (int i = 0; i < MT; ++i) f.x[i] = *reinterpret_cast<const u32x4_t*>(sm.a[st] + a_row + i * 32 * 64 + off);
+    for (int j = 0; j < NT; ++j) {
+      const int c = 32 * j + r;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) f.w[j] = *reinterpret_cast<const u32x4_t*>(sm.b[st] + b_row + j * 32 * 64 + off);
-  };
-  auto read_scales = [&](Scl& c, int s) {
-    const uint8_t* sa_c = sm.sa[(s >> 2) & 1] + 4 * (s & 3);
-    const uint8_t* sb_c = sm.sb[(s >> 2) & 1] + 4 * (s & 3);
+      for (int u = 0; u < 4; ++u)
+        pw[j][u] = *reinterpret_cast<const u32x4_t*>(sm.b[wave] + c * 128 + 16 * ((2 * u + h) ^ ((c >> 1) & 7)));
+      const u32x2_t v = *reinterpret_cast<const u32x2_t*>(sm.sb[(s >> 1) & 1] + 16 * (64 * wave + c) + sc_off);
+      swb[j][0] = v.x >> sh;
+      swb[j][1] = v.y >> sh;
+    }
 #pragma unroll
-    for (int i = 0; i < MT; ++i) c.x[i] = *reinterpret_cast<const uint32_t*>(sa_c + sa_row + i * 32 * 16);
+    for (int i = 0; i < MT; ++i) {
+      const u32x2_t v = *reinterpret_cast<const u32x2_t*>(sm.sa[(s >> 1) & 1] + 16 * (32 * i + r) + sc_off);
+      sxa[i][0] = v.x >> sh;
+      sxa[i][1] = v.y >> sh;
+    }
+    // everything the next stage needs: scale chunk, weight generation, activations
+    if ((s & 1) == 0 && (s >> 1) + 1 < nchunk) issue_scales((s >> 1) + 1);
+    if (s + 1 < nst) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);      // lgkmcnt(0): the copy has read the generation's area
+      issue_b(s + 1);
+      issue_a(s + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // sub-step u: the 32 k of block 2u + h of the stage (16-byte chunk 2u + h
+    // of the row); each sub-step's fragments are read while the previous
+    // sub-step's MFMAs run (two register sets)
+    const uint8_t* la = sm.a[s & 1] + r * 128;
+    u32x4_t fx[2][MT];
+    auto read_fx = [&](u32x4_t (&f)[MT], int u) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) c.w[j] = *reinterpret_cast<const uint32_t*>(sb_c + sb_row + j * 32 * 16);
-  };
-  auto mfmas = [&](const Half& f, const Scl& c, int kk) {
-    const int sh = 8 * (2 * kk + h);
+      for (int i = 0; i < MT; ++i)
+        f[i] = *reinterpret_cast<const u32x4_t*>(la + i * 32 * 128 + 16 * ((2 * u + h) ^ swz));
+    };
+    read_fx(fx[0], 0);
 #pragma unroll
-    for (int i = 0; i < MT; ++i)
+    for (int u = 0; u < 4; ++u) {
+      if (u < 3) read_fx(fx[(u + 1) & 1], u + 1);
 #pragma unroll
       for (int j = 0; j < NT; ++j)
-        acc[i][j] = mfma_w4(f.w[j], f.x[i], (c.w[j] >> sh) & 0xFF, (c.x[i] >> sh) & 0xFF, acc[i][j]);
-  };
-  // Stage s, entered with its sub-step 0 fragments and its scales in
-  // registers (k0, sc): read its sub-step 1 fragments; refill ring slot
-  // (s + 3) % 4 -- stage s - 1's, whose reads every wave finished before the
-  // barrier in the middle of stage s - 1 -- with stage s + 3; sub-step 0's
-  // MFMAs; wait for stage s + 1 and barrier; read stage s + 1's sub-step 0
-  // fragments and scales into (nk0, nsc); sub-step 1's MFMAs.  Each batch of
-  // reads is covered by 8 MFMAs per wave, and the MFMA pipe keeps sub-step
-  // 1's work across the barrier (with one workgroup per CU, a barrier at the
-  // end of the stage drained the pipe every stage).  Stage s's reads all
-  // precede the barrier in its middle, and its slot is refilled only in
-  // stage s + 1.
-  auto stage = [&](const Half& k0, const Scl& sc, Half& nk0, Scl& nsc, int s) {
-    __builtin_amdgcn_sched_barrier(0);
-    Half k1;
-    read_half(k1, s, 1);
-    const bool chunk_start = (s & 3) == 0;
-    if (chunk_start) issue_scales(min((s >> 2) + 1, last_chunk));
-    const bool refill = s + S - 1 <= last;
-    const int nstg = (s + S - 1) & (S - 1);
-    if (refill) issue_codes(nstg, s + S - 1, 0);
-    mfmas(k0, sc, 0);
-    if (refill) issue_codes(nstg, s + S - 1, 1);
-    if (s + 1 <= last) {
-      // stage s+1 (and its scale chunk) have landed once only the transfers
-      // issued after stage s+1's may be in flight: stages s+2 and s+3 (4 ops
-      // each, when they exist) and the scale chunks issued at stages s-1, s
-      const bool c_prev = s >= 1 && ((s - 1) & 3) == 0;
-      const int pend = (s + 2 <= last ? 4 : 0) + (refill ? 4 : 0) + (chunk_start ? 1 : 0) + (c_prev ? 1 : 0);
+#pragma unroll
+        for (int i = 0; i < MT; ++i) {
+          if ((u & 1) == 0)
+            acc[i][j] = mfma_w4<0>(pw[j][u], fx[u & 1][i], swb[j][u >> 1], sxa[i][u >> 1], acc[i][j]);
+          else
+            acc[i][j] = mfma_w4<2>(pw[j][u], fx[u & 1][i], swb[j][u >> 1], sxa[i][u >> 1], acc[i][j]);
+        }
       __builtin_amdgcn_sched_barrier(0);
-      switch (pend) {
-        case 9: wait_vmcnt_barrier<9>(); break;
-        case 8: wait_vmcnt_barrier<8>(); break;
-        case 5: wait_vmcnt_barrier<5>(); break;
-        case 4: wait_vmcnt_barrier<4>(); break;
-        case 1: wait_vmcnt_barrier<1>(); break;
-        default: wait_vmcnt_barrier<0>(); break;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      read_half(nk0, s + 1, 0);
-      read_scales(nsc, s + 1);
     }
-    mfmas(k1, sc, 1);
+    // all the next stage needs has landed (nothing is pending after the last
+    // stage); unconditional, so that the MFMAs above stay ahead of it (behind
+    // a branch the compiler moved them past the wait)
+    __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);   // vmcnt(0)
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
   };
+  for (int s = 0; s < nst; ++s) stage(s);
+  __syncthreads();
+  static_assert(sizeof(W4Smem<BM>) >= (size_t)4 * BM * 128, "epilogue block fits");
+  store_block_lds<MT>(reinterpret_cast<uint8_t*>(&sm) + wave * BM * 128, acc, lane, out, ndim, ti.row0, ti.row_end,
+                      col0 + 64 * wave, ndim);
+}
 
-  const int nst = (int)(kdim / 128);      // >= 4 and even (K % 512 == 0)
-  Half h0, h1;
-  Scl c0, c1;
-  read_half(h0, 0, 0);
-  read_scales(c0, 0);
-  for (int s = 0; s < nst; s += 2) {
-    stage(h0, c0, h1, c1, s);
-    stage(h1, c1, h0, c0, s + 1);
-  }
-  // every wave's fragment reads of the ring are done before any wave stages
-  // its output there (no code transfer is pending: the last one, stage
-  // last's, was waited for in the middle of stage last - 1); drain the
-  // clamped scale transfer too (it lands outside the epilogue block)
-  __builtin_amdgcn_s_waitcnt(0x70 | 0xF00);
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  asm volatile("s_barrier" ::: "memory");
-  static_assert(offsetof(W4Smem, sa) >= (size_t)8 * 128 * 128, "epilogue block fits in front of the scales");
-  store_block_lds<MT>(reinterpret_cast<uint8_t*>(&sm) + wave * 128 * 128, acc, lane, out, ndim, ti.row0 + 128 * wm,
-                      ti.row_end, col0 + wn * 64, ndim);
+__global__ void __launch_bounds__(kW4Threads, 2)
+k_grouped_mm_fwd_w4a4_128(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+                          const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
+                          const int32_t* __restrict__ offs, int experts, int64_t tokens, int64_t ndim, int64_t kdim,
+                          uint8_t* __restrict__ out, int gx) {
+  w4a4_body<128>(xq, xs, packed, scales, offs, experts, tokens, ndim, kdim, out, gx);
+}
+__global__ void __launch_bounds__(kW4Threads, 2)
+k_grouped_mm_fwd_w4a4_96(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+                         const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
+                         const int32_t* __restrict__ offs, int experts, int64_t tokens, int64_t ndim, int64_t kdim,
+                         uint8_t* __restrict__ out, int gx) {
+  w4a4_body<96>(xq, xs, packed, scales, offs, experts, tokens, ndim, kdim, out, gx);
 }
 
 // ------------------------------------------------------------- forward, W4A8
@@ -1657,10 +1680,18 @@ hipError_t launch_grouped_mm_w4a4(const void* xq, const uint8_t* xs, int64_t tok
                                   const uint8_t* scales, int64_t experts, int64_t n, int64_t k, const int32_t* offs,
                                   void* out, hipStream_t st) {
   const int64_t gx = (n + kW4BN - 1) / kW4BN;
-  const int64_t gy = (tokens + kW4BM - 1) / kW4BM + experts;
-  if (!grid_fits(gx * gy, kW4Threads)) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(k_grouped_mm_fwd_w4a4, dim3((unsigned)(gx * gy)), dim3(kW4Threads), 0, st, (const uint8_t*)xq, xs,
-                     (const uint8_t*)packed, scales, offs, (int)experts, tokens, n, k, (uint8_t*)out, (int)gx);
+  // 96-row tiles when they take no more rounds of two workgroups per CU (as the bf16 forward)
+  const int cus = device_cus();
+  const int64_t slots = 2 * (int64_t)(cus > 0 ? cus : 256);
+  const int64_t n128 = gx * ((tokens + 127) / 128 + experts), n96 = gx * ((tokens + 95) / 96 + experts);
+  const bool bm96 = (n96 + slots - 1) / slots <= (n128 + slots - 1) / slots;
+  if (!grid_fits(bm96 ? n96 : n128, kW4Threads)) return hipErrorInvalidConfiguration;
+  if (bm96)
+    hipLaunchKernelGGL(k_grouped_mm_fwd_w4a4_96, dim3((unsigned)n96), dim3(kW4Threads), 0, st, (const uint8_t*)xq, xs,
+                       (const uint8_t*)packed, scales, offs, (int)experts, tokens, n, k, (uint8_t*)out, (int)gx);
+  else
+    hipLaunchKernelGGL(k_grouped_mm_fwd_w4a4_128, dim3((unsigned)n128), dim3(kW4Threads), 0, st, (const uint8_t*)xq,
+                       xs, (const uint8_t*)packed, scales, offs, (int)experts, tokens, n, k, (uint8_t*)out, (int)gx);
   return hipGetLastError();
 }
 
