@@ -5,9 +5,11 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every data pointer is DEVICE memory owned by the caller.  The library
- *    never allocates, frees or synchronizes; each call enqueues its kernels on
- *    `stream` (a hipStream_t passed as void*; NULL = the null stream) and
- *    returns immediately.
+ *    never allocates or frees device memory and never synchronizes; each
+ *    call enqueues its kernels on `stream` (a hipStream_t passed as void*;
+ *    NULL = the null stream) and returns immediately.  The one exception is
+ *    the debug check mxq_validate_offs, which copies into host memory of its
+ *    own and waits for the stream.
  *  - Tensors are dense and row-major; leading dimensions are flattened into
  *    `rows` by the caller.  Any alignment is accepted (misaligned or oddly
  *    shaped tensors take a slower general kernel).
