@@ -469,12 +469,23 @@ def low_bit_summary(legs, K, prefix, peak):
             "legs": f"{prefix}.gate_up + {prefix}.down forwards ({enc} of the activations + block-scaled MFMA GEMM)"}
 
 
+def source_code_hash(path):
+    """sha256 of a C++/HIP source with its comments removed and whitespace
+    collapsed: the code the counters were taken on, not its wording."""
+    import hashlib
+    import re
+    with open(path, encoding="utf-8") as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return hashlib.sha256(" ".join(src.split()).encode()).hexdigest()
+
+
 def measured_traffic(kernel):
     """Bytes per launch of `kernel` past L2 (to Infinity Cache / HBM) from the
     committed counter summary (rocprofv3 FETCH_SIZE and WRITE_SIZE, scaled by
     what they read for the copy kernel), averaged over the launches the bench
-    makes, or None when there is none or the kernel source changed since."""
-    import hashlib
+    makes, or None when there is none or the kernel code changed since."""
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", "traffic.json")
     try:
@@ -485,9 +496,8 @@ def measured_traffic(kernel):
     k = rec.get("kernels", {}).get(kernel)
     if not k:
         return None
-    with open(os.path.join(here, k["source"]), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != k["source_sha256"]:
-            return None
+    if source_code_hash(os.path.join(here, k["source"])) != k["source_code_sha256"]:
+        return None
     return {"bytes_per_launch": k["bytes_per_launch"], "fetch_bytes": k["fetch_bytes"],
             "write_bytes": k["write_bytes"], "unit": "bytes",
             "fetch_factor": rec.get("calibration", {}).get("fetch_factor"), "from": "profiles/traffic.json"}

@@ -911,8 +911,9 @@ k_grouped_mm_fwd_fl96(const uint8_t* __restrict__ a, const uint8_t* __restrict__
 // reference, to fp32 rounding): lane l carries row (or column) l % 32 and
 // the 32 consecutive k of block l / 32 of the 64-k sub-step, two codes per
 // byte with the even k in the low nibble -- exactly one stored row segment
-// and its E8M0 block -- and byte 0 of its scale register scales that block
-// (a 0xFF scale gives NaN).  So no code is decoded here: both operands go
+// and its E8M0 block -- and the byte of its scale register that the
+// instruction's byte select names scales that block (a 0xFF scale gives
+// NaN).  So no code is decoded here: both operands go
 // from global memory through LDS into the MFMA as stored.  Products of two
 // e2m1 codes and two power-of-two scales are exact, sums run in fp32, the
 // output rounds to bf16 nearest-even.
@@ -934,8 +935,8 @@ k_grouped_mm_fwd_fl96(const uint8_t* __restrict__ a, const uint8_t* __restrict__
 //    right by 8h, so the block of sub-step u sits in byte 2(u & 1) of dword
 //    u / 2).
 // A stage is 4 MFMA sub-steps of 64 k: per wave and stage the same bytes of
-// LDS traffic per MFMA cycle as the W4A8 kernel's 128-k stage (24 fp4 MFMAs
-// of 32 cycles against 12 fp8 x fp4 MFMAs of 64).  Each stage issues
+// LDS traffic per MFMA cycle as the W4A8 kernel's 128-k stage (at 96 rows,
+// 24 fp4 MFMAs of 32 cycles against 12 fp8 x fp4 MFMAs of 64).  Each stage issues
 // everything the next needs (scale chunk, weight generation, activation
 // stage) and ends by waiting for it (vmcnt(0)) and the barrier.  Needs
 // K % 512 == 0.
