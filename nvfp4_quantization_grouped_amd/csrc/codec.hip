@@ -532,9 +532,9 @@ __device__ __forceinline__ uint32_t nvfp4_block_scale_fast(float ab, float g, co
 // fl(x / d), which is -0.0 (code 0) for a negative x with |x / d| <= 2^-150,
 // a boundary the reciprocal product cannot see; with d < 256 only nonzero
 // fp32 subnormal inputs are that small (bf16 and f16 values are not).  So
-// chunks with an element within reach of a midpoint (exact ties among them),
-// with d >= 256 or a reciprocal past 2^126, or with a nonzero fp32 subnormal
-// input take IEEE divisions.
+// an element within reach of a midpoint (exact ties among them) takes an
+// IEEE division, and chunks with d >= 256 or a reciprocal past 2^126, or
+// with a nonzero fp32 subnormal input, take IEEE divisions for all eight.
 template <int DT>
 __device__ __forceinline__ uint32_t nvfp4_encode_chunk(const Chunk<DT>& ch, float d) {
   float v[8];
@@ -567,14 +567,32 @@ __device__ __forceinline__ uint32_t nvfp4_encode_chunk(const Chunk<DT>& ch, floa
 #pragma unroll
     for (int i = 0; i < 8; ++i) exact |= ((as_u32(v[i]) & 0x7FFFFFFFu) - 1u) < 0x007FFFFFu;   // nonzero subnormal
   }
-  if (lo == hi && !exact) return lo;
-  // (+ 0.0f: a quotient that underflows to -0.0 gets code 0)
-  uint32_t c = 0;
-  c = enc_fp4_f2<0>(c, v[0] / d + 0.0f, v[1] / d + 0.0f, 1.0f);
-  c = enc_fp4_f2<1>(c, v[2] / d + 0.0f, v[3] / d + 0.0f, 1.0f);
-  c = enc_fp4_f2<2>(c, v[4] / d + 0.0f, v[5] / d + 0.0f, 1.0f);
-  c = enc_fp4_f2<3>(c, v[6] / d + 0.0f, v[7] / d + 0.0f, 1.0f);
-  return c;
+  if (exact) {
+    // (+ 0.0f: a quotient that underflows to -0.0 gets code 0)
+    uint32_t c = 0;
+    c = enc_fp4_f2<0>(c, v[0] / d + 0.0f, v[1] / d + 0.0f, 1.0f);
+    c = enc_fp4_f2<1>(c, v[2] / d + 0.0f, v[3] / d + 0.0f, 1.0f);
+    c = enc_fp4_f2<2>(c, v[4] / d + 0.0f, v[5] / d + 0.0f, 1.0f);
+    c = enc_fp4_f2<3>(c, v[6] / d + 0.0f, v[7] / d + 0.0f, 1.0f);
+    return c;
+  }
+  // The bracket decides each element on its own: where its two codes
+  // agree, that is the code.  Only the elements whose codes differ take
+  // the division, one element position per branch, so a wave pays for a
+  // division at a position only when one of its lanes straddles a midpoint
+  // there.  (Exact ties are common: with x in bf16 and d = s_b g, a tensor
+  // maximum whose odd part shares a factor with 2688 = 2^7 * 3 * 7 puts
+  // quotients on midpoints in up to 3% of the chunks, in most waves.)
+  const uint32_t diff = lo ^ hi;
+  if (diff != 0u) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((diff >> (4 * i)) & 0xFu) {
+        const uint32_t nib = enc_fp4_f2<0>(0u, v[i] / d + 0.0f, 0.0f, 1.0f) & 0xFu;
+        lo = (lo & ~(0xFu << (4 * i))) | (nib << (4 * i));
+      }
+  }
+  return lo;
 }
 
 template <int DT, class M>
@@ -734,8 +752,8 @@ __global__ void __launch_bounds__(kThreads) k_dequantize_nvfp4_general(const uin
 // per block; d and its reciprocal are wave-uniform.  The error needs only the
 // code magnitudes, which the reciprocal bracket of nvfp4_encode_chunk gives
 // (x times rcp(d)(1 -+ 2^-20): where the two codes agree, no midpoint lies
-// between them); lanes whose bracket straddles a midpoint take divisions.
-// The stored codes are then encoded as the max rule's are.
+// between them); elements whose bracket straddles a midpoint take a
+// division each.  The stored codes are then encoded as the max rule's are.
 
 // Squared error of 8 elements (v) whose codes are the dword c, under d; adds
 // into err in element order.  The residual is one fused multiply-add; the
@@ -769,13 +787,26 @@ __device__ __forceinline__ uint32_t sweep_codes8(const float* v, float rd, float
   hi = enc_fp4_f2<2>(hi, v[4] * ru, v[5] * ru, 1.0f);
   lo = enc_fp4_f2<3>(lo, v[6] * rd, v[7] * rd, 1.0f);
   hi = enc_fp4_f2<3>(hi, v[6] * ru, v[7] * ru, 1.0f);
-  if (lo == hi && !force_exact) return lo;
-  uint32_t c = 0;
-  c = enc_fp4_f2<0>(c, v[0] / d, v[1] / d, 1.0f);
-  c = enc_fp4_f2<1>(c, v[2] / d, v[3] / d, 1.0f);
-  c = enc_fp4_f2<2>(c, v[4] / d, v[5] / d, 1.0f);
-  c = enc_fp4_f2<3>(c, v[6] / d, v[7] / d, 1.0f);
-  return c;
+  if (force_exact) {
+    uint32_t c = 0;
+    c = enc_fp4_f2<0>(c, v[0] / d, v[1] / d, 1.0f);
+    c = enc_fp4_f2<1>(c, v[2] / d, v[3] / d, 1.0f);
+    c = enc_fp4_f2<2>(c, v[4] / d, v[5] / d, 1.0f);
+    c = enc_fp4_f2<3>(c, v[6] / d, v[7] / d, 1.0f);
+    return c;
+  }
+  // per element, as in nvfp4_encode_chunk: only positions whose two codes
+  // differ take the division
+  const uint32_t diff = lo ^ hi;
+  if (diff != 0u) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((diff >> (4 * i)) & 0xFu) {
+        const uint32_t nib = enc_fp4_f2<0>(0u, v[i] / d, 0.0f, 1.0f) & 0xFu;
+        lo = (lo & ~(0xFu << (4 * i))) | (nib << (4 * i));
+      }
+  }
+  return lo;
 }
 
 template <int DT>

@@ -85,6 +85,19 @@ def test_exact_ties_and_zero_tensor():
     assert g.item() == 0.0 and torch.all(s.view(torch.uint8) == 0x38) and torch.all(p == 0)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_tensor_max_sharing_a_factor_with_2688(dtype):
+    """A tensor max of 91 * 2^-4 (odd part 7 * 13; 2688 = 2^7 * 3 * 7) puts
+    many quotients x / d exactly on e2m1 midpoints: in bf16 about 3% of the
+    chunks hold one, beside elements the reciprocal bracket decides, so
+    chunks mix both kinds (the block pass divides only where the bracket
+    straddles).  Whole [1024, 2048] tensor."""
+    g = np.random.default_rng(91)
+    v = np.clip(g.standard_normal((1024, 2048)), -5.5, 5.5) * 2.0 ** (g.integers(-3, 1, size=(1024, 1)))
+    v[17, 5] = 91.0 / 16.0
+    check_all(bits_of(v.astype(np.float32), dtype), dtype, f"max 91/16 {dtype}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_misaligned_buffers_take_the_general_path(dtype):
     rows, k = 37, 96
