@@ -459,21 +459,21 @@ __device__ __forceinline__ void nvfp4_amax_publish(uint32_t m, uint32_t* __restr
 template <int DT, class M>
 __global__ void __launch_bounds__(kThreads) k_nvfp4_amax(const uint8_t* __restrict__ x, int64_t nchunks,
                                                        uint32_t* __restrict__ slot) {
+  // Branch-free loads: a lane past the end reads the last chunk again and
+  // leaves it out of the max.  With the loads behind `c < nchunks` the
+  // compiler moved each chunk's max into its branch, after a vmcnt(0), so a
+  // lane had one load in flight instead of kUnroll.
   uint32_t m = 0;
-  const int64_t step = (int64_t)gridDim.x * kThreads * M::kUnroll;
+  const int64_t step = (int64_t)gridDim.x * kThreads * M::kUnroll, last = nchunks - 1;
   for (int64_t base = (int64_t)blockIdx.x * kThreads * M::kUnroll; base < nchunks; base += step) {
     Chunk<DT> ch[M::kUnroll];
 #pragma unroll
+    for (int u = 0; u < M::kUnroll; ++u) load_chunk<DT, M>(x, min(base + u * kThreads + threadIdx.x, last), ch[u]);
+#pragma unroll
     for (int u = 0; u < M::kUnroll; ++u) {
-      const int64_t c = base + u * kThreads + threadIdx.x;
-      if (c < nchunks) load_chunk<DT, M>(x, c, ch[u]);
-      else {
-#pragma unroll
-        for (int i = 0; i < Chunk<DT>::kWords; ++i) ch[u].w[i] = 0u;
-      }
+      const uint32_t a = chunk_amax_bits<DT>(ch[u]);
+      m = max(m, base + u * kThreads + threadIdx.x <= last ? a : 0u);
     }
-#pragma unroll
-    for (int u = 0; u < M::kUnroll; ++u) m = max(m, chunk_amax_bits<DT>(ch[u]));
   }
   nvfp4_amax_publish(m, slot);
 }
