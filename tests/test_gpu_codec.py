@@ -269,3 +269,12 @@ def test_empty_inputs():
     assert p.shape == (0, 32) and s.shape == (0, 2)
     assert mxq.dequantize_mxfp4(p, s, torch.float32).shape == (0, 64)
     assert mxq.quantize_cache(z, "nvfp4", 16).shape == (0, 64)
+    for fmt, bs, cw in (("fp8", 32, 64), ("mxfp4", 32, 32), ("nvfp4", 16, 32)):
+        c, sc = mxq.quantize_cache_packed(z, fmt, bs)
+        assert c.shape == (0, cw) and sc.shape == (0, 64 // bs)
+        assert mxq.dequantize_cache_packed(c, sc, fmt, bs, torch.bfloat16).shape == (0, 64)
+    # two-level NVFP4 of an empty tensor: no launch (the library leaves g alone; the binding starts it at 0)
+    for q in (mxq.quantize_nvfp4, mxq.quantize_nvfp4_mse):
+        p2, s2, g2 = q(z)
+        assert p2.shape == (0, 32) and s2.shape == (0, 4) and g2.item() == 0.0
+        assert mxq.dequantize_nvfp4(p2, s2, g2, torch.bfloat16).shape == (0, 64)

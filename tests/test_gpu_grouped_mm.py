@@ -320,3 +320,64 @@ def test_validate_offs():
     assert check([5, 70, 60], 64) == 1
     assert check(list(range(0, 4000, 2)), 3998) == -1          # many experts
     assert check(list(range(0, 4000, 2)), 3996) == 1999
+
+
+def test_degenerate_shapes_write_zeros():
+    """Every grouped-GEMM entry point, through the C-ABI, on the shapes with
+    nothing to reduce or no owning expert: zero experts, an empty reduction
+    (k = 0 for the forwards, n = 0 for grad_x) and offsets that cover no row
+    write an all-zero output; zero tokens launch nothing and succeed."""
+    L = mxq.lib()
+    st = torch.cuda.current_stream().cuda_stream
+    T, N, K, E = 300, 288, 512, 3          # N is grad_x's output width: a multiple of 32
+    g = np.random.default_rng(12)
+    packed, scales = gpu_weights(*synth.packed_weights(*synth.streams(12, 2), E, N, K))
+    packed_t, scales_t = gpu_weights(*synth.packed_weights(*synth.streams(13, 2), E, K, N))   # W_e [K, N] for grad_x
+    x = to_gpu_bits(synth.normal_bf16(g, (T, K)), "bf16")
+    go = to_gpu_bits(synth.normal_bf16(g, (T, K)), "bf16")
+    xq = torch.from_numpy(g.integers(0, 256, (T, K // 2), dtype=np.uint8)).to(dev())
+    x8 = torch.from_numpy(g.integers(0, 0x70, (T, K), dtype=np.uint8)).to(dev())
+    xs = torch.from_numpy(g.integers(120, 130, (T, K // 32), dtype=np.uint8)).to(dev())
+    none = torch.zeros(E, dtype=torch.int32, device=dev())
+    some = torch.tensor([100, 200, 300], dtype=torch.int32, device=dev())
+
+    def fresh(cols):
+        return torch.full((T, cols), 7.0, dtype=torch.bfloat16, device=dev())
+
+    def run(name, out, *args):
+        assert getattr(L, name)(*args, st) == 0, name
+        torch.cuda.synchronize()
+        assert torch.all(out.float() == 0), f"{name}: output not all zero"
+
+    for e, offs in ((0, some), (E, none)):
+        y = fresh(N)
+        run("mxfp4_grouped_mm_fwd", y, x.data_ptr(), T, K, packed.data_ptr(), scales.data_ptr(), e, N,
+            offs.data_ptr(), y.data_ptr())
+        y = fresh(N)
+        run("mxfp4_grouped_mm_fwd_w4a4", y, xq.data_ptr(), xs.data_ptr(), T, K, packed.data_ptr(), scales.data_ptr(),
+            e, N, offs.data_ptr(), y.data_ptr())
+        y = fresh(N)
+        run("mxfp4_grouped_mm_fwd_w4a8", y, x8.data_ptr(), xs.data_ptr(), T, K, packed.data_ptr(), scales.data_ptr(),
+            e, N, offs.data_ptr(), y.data_ptr())
+        gx = fresh(N)
+        run("mxfp4_grouped_mm_bwd_x", gx, go.data_ptr(), T, K, packed_t.data_ptr(), scales_t.data_ptr(), e, N,
+            offs.data_ptr(), gx.data_ptr())
+    # an empty reduction
+    y = fresh(N)
+    run("mxfp4_grouped_mm_fwd", y, x.data_ptr(), T, 0, packed.data_ptr(), scales.data_ptr(), E, N, some.data_ptr(),
+        y.data_ptr())
+    for name, a in (("mxfp4_grouped_mm_fwd_w4a4", xq), ("mxfp4_grouped_mm_fwd_w4a8", x8)):
+        y = fresh(N)
+        run(name, y, a.data_ptr(), xs.data_ptr(), T, 0, packed.data_ptr(), scales.data_ptr(), E, N, some.data_ptr(),
+            y.data_ptr())
+    gx = fresh(N)
+    run("mxfp4_grouped_mm_bwd_x", gx, go.data_ptr(), T, 0, packed_t.data_ptr(), scales_t.data_ptr(), E, N,
+        some.data_ptr(), gx.data_ptr())
+    # zero tokens: nothing launched, the output untouched
+    y = fresh(N)
+    assert L.mxfp4_grouped_mm_fwd(x.data_ptr(), 0, K, packed.data_ptr(), scales.data_ptr(), E, N, some.data_ptr(),
+                                  y.data_ptr(), st) == 0
+    assert L.mxfp4_grouped_mm_bwd_x(go.data_ptr(), 0, K, packed_t.data_ptr(), scales_t.data_ptr(), E, N,
+                                    some.data_ptr(), y.data_ptr(), st) == 0
+    torch.cuda.synchronize()
+    assert torch.all(y.float() == 7.0)
