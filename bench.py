@@ -15,9 +15,10 @@ workload, all inputs already resident in HBM:
   of each (codes + scale bytes) and its dequantize-on-read;
 * bulk bf16 [65536, 7168]: quantize_mxfp4, dequantize_mxfp4, quantize_cache
   nvfp4/16, fp8/128 and mxfp4/32, two-level NVFP4 quantize and dequantize;
-  the NVFP4 MSE block-scale sweep of a bf16 weight [4096, 7168] (VALU-bound:
-  reported against the fp32 issue rate, 6 operations per element and
-  candidate); dequantization of a 2^30-parameter mxfp4 weight
+  the NVFP4 MSE block-scale sweep of a bf16 weight [4096, 7168] (reported
+  as the rule's operation rate, 6 per element and candidate over all 126
+  candidates: the kernel skips the candidates an exact bound rules out, so
+  no roofline fraction applies); dequantization of a 2^30-parameter mxfp4 weight
   [64, 4096, 4096] to bf16;
 * mxfp4 round trip of an fp32 [256, 1024] tensor (latency-bound).
 
@@ -41,10 +42,6 @@ HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 MFMA_FP4_PEAK_TFLOPS = 10100.0   # MI355X dense fp4 (MXFP4) MFMA
 MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
-# fp32 VALU issue rate without packed (two-wide) fp32 or FMA pairing: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
-ALU_FP32_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
-# MI355X's published fp32 vector peak (packed two-wide FMAs, two flops each): 4x the issue rate above
-FP32_PUBLISHED_TFLOPS = 157.3
 METRIC = "quant/dequant GB/s (% HBM peak); MXFP4 grouped-GEMM TFLOP/s (% MFMA peak)"
 
 
@@ -59,9 +56,9 @@ def parse():
 
 
 class Leg:
-    def __init__(self, name, kernel, kind, work, fn, reps=1, peak=None, alu_ops=None):
+    def __init__(self, name, kernel, kind, work, fn, reps=1, peak=None, rule_ops=None):
         self.name, self.kernel, self.kind, self.work, self.fn, self.reps = name, kernel, kind, work, fn, reps
-        self.alu_ops = alu_ops   # algorithmic fp32 operations per call, for a VALU-bound leg
+        self.rule_ops = rule_ops   # fp32 operations per call of an exhaustive search rule (all candidates)
         # the roof this leg's rate is a fraction of (TFLOP/s or GB/s)
         self.peak = peak or (MFMA_BF16_PEAK_TFLOPS if kind == "flop" else HBM_PEAK_GBPS)
         self.ms = 0.0   # summed event time over the timed steps
@@ -286,8 +283,8 @@ def main():
         legs.append(Leg("bulk.dequantize_nvfp4", "k_dequantize_nvfp4<bf16>", "byte", nb * (0.5 + 1 / 16 + 2),
                         lambda i: check(L.dequantize_nvfp4(npk.data_ptr(), nsc.data_ptr(), ng.data_ptr(), br, bc,
                                                            bdq.data_ptr(), 1, sp), "dqnv")))
-        # MSE block-scale sweep of one bf16 weight [4096, 7168]: 126 candidate scales per block of 16,
-        # bound by VALU throughput (bytes: the amax read + the sweep read + outputs)
+        # MSE block-scale sweep of one bf16 weight [4096, 7168]: 126 candidate scales per block of 16
+        # (bytes: the amax read + the sweep read + outputs)
         nvw = bf16(synth.nvfp4_weight(seed=0)["w"])
         mr, mc = nvw.shape
         mpk = torch.empty(mr, mc // 2, dtype=torch.uint8, device=dev)
@@ -296,7 +293,7 @@ def main():
         legs.append(Leg("bulk.quantize_nvfp4_mse", "k_nvfp4_amax+k_quantize_nvfp4_mse<bf16>", "byte",
                         nvw.numel() * (2 * 2 + 0.5 + 1 / 16),
                         lambda i: check(L.quantize_nvfp4_mse(nvw.data_ptr(), 1, mr, mc, mpk.data_ptr(), msc.data_ptr(),
-                                                             mg.data_ptr(), sp), "qmse"), alu_ops=6.0 * 126 * nvw.numel()))
+                                                             mg.data_ptr(), sp), "qmse"), rule_ops=6.0 * 126 * nvw.numel()))
         nw = 64 * 4096 * 4096
         legs.append(Leg("bulk.weight_dequant", "k_dequantize_mxfp4<bf16>", "byte", nw * (0.5 + 1 / 32 + 2),
                         lambda i: check(L.dequantize_mxfp4(wp.data_ptr(), ws.data_ptr(), 64 * 4096, 4096,
@@ -356,10 +353,13 @@ def main():
         else:
             rate = leg.work / (per_call_ms * 1e-3) / 1e9
             d.update({"GB": round(leg.work / 1e9, 4), "GB/s": round(rate, 1), "frac_hbm": round(rate / HBM_PEAK_GBPS, 4)})
-        if leg.alu_ops:
-            tops = leg.alu_ops / (per_call_ms * 1e-3) / 1e12
-            d.update({"bound": "alu", "Tops/s": round(tops, 2), "frac_alu": round(tops / ALU_FP32_PEAK_TOPS, 4),
-                      "frac_fp32_published": round(tops / FP32_PUBLISHED_TFLOPS, 4)})
+        if leg.rule_ops:
+            # the rule's work over the event time; the kernel skips candidates an exact lower bound
+            # rules out, so this rate can pass the fp32 issue rate and has no roofline fraction
+            d.update({"bound": "alu", "rule_Tops/s": round(leg.rule_ops / (per_call_ms * 1e-3) / 1e12, 2),
+                      "rule_ops_per_call": leg.rule_ops})
+            for k in ("GB/s", "frac_hbm"):
+                d.pop(k, None)
         out_legs.append(d)
 
     moe_legs = [l for l in legs if l.name.startswith("moe.")]
@@ -380,7 +380,7 @@ def main():
         ms = sum(l.ms for l in ls) / K
         return b / (ms * 1e-3) / 1e9 if ms > 0 else None
 
-    codec = [l for l in legs if l.kind == "byte" and not l.alu_ops and not l.name.startswith(("roundtrip", "w4a4.", "w4a8."))]
+    codec = [l for l in legs if l.kind == "byte" and not l.rule_ops and not l.name.startswith(("roundtrip", "w4a4.", "w4a8."))]
     hbm_gbps = aggregate([l for l in codec if not is_next(l)])
     hbm_next_gbps = aggregate([l for l in codec if is_next(l)])
 

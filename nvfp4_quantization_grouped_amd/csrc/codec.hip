@@ -748,12 +748,21 @@ __global__ void __launch_bounds__(kThreads) k_dequantize_nvfp4_general(const uin
 // E4M3 values (codes 0x01 .. 0x7E, in order) as its scale and keeps the first
 // with the least fp32 squared error sum(fl(e^2)), e = x - e2m1(fl(x / d)) d in
 // one fused multiply-add, d = fl(s g), squares and sums rounded one by one,
-// elements in order.  One lane
-// per block; d and its reciprocal are wave-uniform.  The error needs only the
-// code magnitudes, which the reciprocal bracket of nvfp4_encode_chunk gives
-// (x times rcp(d)(1 -+ 2^-20): where the two codes agree, no midpoint lies
+// elements in order.  One lane per block.  The error needs only the code
+// magnitudes, which the reciprocal bracket of nvfp4_encode_chunk gives (x
+// times rcp(d)(1 -+ 2^-20): where the two codes agree, no midpoint lies
 // between them); elements whose bracket straddles a midpoint take a
 // division each.  The stored codes are then encoded as the max rule's are.
+//
+// Candidates that cannot win are skipped without changing the result: the
+// terms are non-negative and rounding to nearest is monotone, so a
+// candidate's error is at least any one of its terms, computed the same way.
+// The lane first evaluates the max rule's scale in full, then computes the
+// term of the block's largest element under every candidate (wave-uniform
+// d), and evaluates in full only the candidates whose term is below the
+// best error so far (or equal to it at a lower code: the first candidate
+// with the least error wins, so the selection keeps the least (error, code)
+// pair).  On normally distributed weights about a fifth of the 126 survive.
 
 // Squared error of 8 elements (v) whose codes are the dword c, under d; adds
 // into err in element order.  The residual is one fused multiply-add; the
@@ -809,6 +818,33 @@ __device__ __forceinline__ uint32_t sweep_codes8(const float* v, float rd, float
   return lo;
 }
 
+// The term of one element under d: its code as sweep_codes8 chooses it
+// (returned in *code), then the squared residual as sweep_err8 forms it
+// (returned in *res before squaring).
+__device__ __forceinline__ float sweep_term1(float x, float d, uint32_t* code, float* res) {
+  const float r = __builtin_amdgcn_rcpf(d);
+  const bool force_exact = !(r <= 0x1p126f);
+  const uint32_t lo = enc_fp4_f2<0>(0u, x * (r * (1.0f - 0x1p-20f)), 0.0f, 1.0f) & 0xFu;
+  const uint32_t hi = enc_fp4_f2<0>(0u, x * (r * (1.0f + 0x1p-20f)), 0.0f, 1.0f) & 0xFu;
+  const uint32_t c = (force_exact || lo != hi) ? enc_fp4_f2<0>(0u, x / d, 0.0f, 1.0f) & 0xFu : lo;
+  const float e = __builtin_fmaf(-__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0)[0], d, x);
+  *code = c;
+  *res = e;
+  return mul_f32(e, e);
+}
+
+// Squared error of the block v under candidate code (d = its E4M3 value
+// times g, nonzero).
+__device__ __forceinline__ float sweep_err16(const float* v, uint32_t code, float g) {
+  const float d = dec_fp8_f2<false>(code, 1.0f).x * g;
+  const float r = __builtin_amdgcn_rcpf(d);
+  const bool force_exact = !(r <= 0x1p126f);
+  const float rd = r * (1.0f - 0x1p-20f), ru = r * (1.0f + 0x1p-20f);
+  const uint32_t c0 = sweep_codes8(v, rd, ru, d, force_exact);
+  const uint32_t c1 = sweep_codes8(v + 8, rd, ru, d, force_exact);
+  return sweep_err8(v + 8, c1, d, sweep_err8(v, c0, d, 0.0f));
+}
+
 template <int DT>
 __global__ void __launch_bounds__(kThreads) k_quantize_nvfp4_mse(const uint8_t* __restrict__ x,
                                                                uint8_t* __restrict__ packed,
@@ -821,18 +857,58 @@ __global__ void __launch_bounds__(kThreads) k_quantize_nvfp4_mse(const uint8_t* 
     for (int i = 0; i < 16; ++i) v[i] = load_elem<DT>(x, b * 16 + i) + 0.0f;
     uint32_t best = 0x38, w0 = 0, w1 = 0;
     if (g != 0.0f) {
-      best = 0;
+      // the block's largest magnitude (its first element of that magnitude)
+      float xm = v[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) xm = __builtin_fabsf(v[i]) > __builtin_fabsf(xm) ? v[i] : xm;
+      // the max rule's scale first (any candidate would do; this one is near the optimum)
+      uint32_t c_init = enc_fp8_f2<false>(0u, __builtin_fabsf(xm) / (6.0f * g), 0.0f, 1.0f) & 0x7Fu;
+      c_init = c_init < 1u ? 1u : (c_init > 0x7Eu ? 0x7Eu : c_init);
+      best = 0;                                      // 0: no candidate yet
       float best_err = 0.0f;
-      for (uint32_t code = 1; code < 0x7F; ++code) {
+      if (dec_fp8_f2<false>(c_init, 1.0f).x * g != 0.0f) {
+        best = c_init;
+        best_err = sweep_err16(v, c_init, g);
+      }
+      // the codes whose largest-element term does not rule them out, scanned
+      // outwards from c_init.  d grows with the code.  Downwards the scan
+      // stops at an underflowed divisor (every lower one underflows too) or
+      // once the largest element saturates at 6 with 6d <= |xm| and a term
+      // above the best error: every lower code saturates it too, with a
+      // residual |xm| - 6d at least as large.  Upwards it stops after the
+      // first code whose largest element quantizes to 0: every element does,
+      // so every higher code has the same error (sum of x^2) at a higher code.
+      uint32_t keep[4] = {0u, 0u, 0u, 0u};
+      auto consider = [&](uint32_t code, float t) __attribute__((always_inline)) {
+        if (best == 0 || t < best_err || (t == best_err && code < best)) keep[code >> 5] |= 1u << (code & 31);
+      };
+      for (uint32_t code = c_init - 1; code >= 1; --code) {
         const float d = dec_fp8_f2<false>(code, 1.0f).x * g;
-        if (d == 0.0f) continue;                     // the divisor underflowed: not a candidate
-        const float r = __builtin_amdgcn_rcpf(d);
-        const bool force_exact = !(r <= 0x1p126f);
-        const float rd = r * (1.0f - 0x1p-20f), ru = r * (1.0f + 0x1p-20f);
-        const uint32_t c0 = sweep_codes8(v, rd, ru, d, force_exact);
-        const uint32_t c1 = sweep_codes8(v + 8, rd, ru, d, force_exact);
-        const float err = sweep_err8(v + 8, c1, d, sweep_err8(v, c0, d, 0.0f));
-        if (best == 0 || err < best_err) { best = code; best_err = err; }
+        if (d == 0.0f) break;
+        uint32_t cm;
+        float e;
+        const float t = sweep_term1(xm, d, &cm, &e);
+        if (best != 0 && (cm & 7u) == 7u && (e > 0.0f) == (xm > 0.0f) && t > best_err) break;
+        consider(code, t);
+      }
+      for (uint32_t code = c_init + 1; code < 0x7F; ++code) {
+        const float d = dec_fp8_f2<false>(code, 1.0f).x * g;
+        if (d == 0.0f) continue;                     // an underflowed divisor is not a candidate
+        uint32_t cm;
+        float e;
+        const float t = sweep_term1(xm, d, &cm, &e);
+        consider(code, t);
+        if ((cm & 7u) == 0u) break;
+      }
+      // full evaluation of the survivors, lowest code first, per lane
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        while (keep[q] != 0u) {
+          const uint32_t code = 32u * q + (uint32_t)__builtin_ctz(keep[q]);
+          keep[q] &= keep[q] - 1u;
+          const float err = sweep_err16(v, code, g);
+          if (best == 0 || err < best_err || (err == best_err && code < best)) { best = code; best_err = err; }
+        }
       }
       const float d = dec_fp8_f2<false>(best, 1.0f).x * g;
       Chunk<DT_F32> h0, h1;

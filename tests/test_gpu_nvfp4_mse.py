@@ -62,6 +62,36 @@ def test_exact_ties_zero_blocks_and_zero_tensor():
     check(zb, "bf16", "mse all-zero tensor")
 
 
+def test_overflowing_errors_and_repeated_maxima():
+    """Blocks whose squared errors overflow fp32 under most candidates (the
+    sweep then ties at infinity and keeps the first code), blocks whose
+    largest magnitude appears more than once with both signs, blocks of one
+    repeated value, and single-value blocks that many candidates represent
+    exactly (zero-error ties)."""
+    g = np.random.default_rng(77)
+    big = (g.uniform(-1.0, 1.0, (8, 64)) * 3.0e38).astype(np.float32)
+    big[1, :16] = 3.0e38
+    big[1, 16:32] = -3.0e38
+    big[2] = (g.uniform(-1.0, 1.0, 64) * 1.0e20).astype(np.float32)
+    big[3, 32:48] = 0.0
+    big[3, 40] = 6.0 * 2.0 ** 100
+    check(big.view(np.uint32), "f32", "mse overflowing errors")
+    x = g.standard_normal((16, 64)).astype(np.float32)
+    for b in range(x.size // 16):
+        blk = x.reshape(-1, 16)[b]
+        m = np.float32(1.5) * np.abs(blk).max()
+        blk[b % 16] = m
+        blk[(b + 5) % 16] = -m
+        if b % 7 == 0:
+            blk[:] = m
+        if b % 11 == 0:
+            blk[:] = 0.0
+            blk[b % 16] = np.float32(3.0 * 2.0 ** (b % 5 - 2))
+    for dtype in ("f32", "bf16"):
+        xb = x.view(np.uint32) if dtype == "f32" else (x.view(np.uint32) >> 16).astype(np.uint16)
+        check(xb, dtype, f"mse repeated maxima {dtype}")
+
+
 def test_misaligned_input():
     rows, k = 21, 96
     xb = normal_blocks(43, rows, k, "bf16")
