@@ -1601,16 +1601,22 @@ k_grouped_mm_fwd_w4a8(const uint8_t* __restrict__ xq, const uint8_t* __restrict_
 //  * MFMA fragments as in the forward: lane-half h covers n in
 //    [32h, 32h + 32) of the step, sub-step kk the 8 values 32h + 8kk ..;
 //  * Wd's 16-byte chunk c of row n sits at chunk c ^ swz(n), swz(n) =
-//    4 * ((n >> 1) & 1) + ((n >> 1) & 3): the piece writes (8 consecutive
-//    rows, both column halves, one chunk each) and the transposing reads
-//    (4 consecutive rows, one aligned quad of chunks) hit distinct 16-byte
-//    groups of the 64 LDS banks.
+//    (n & 3) + 4 * ((n >> 1) & 1).  A 16-byte LDS write serves 8 lanes (128
+//    bytes) per cycle, a transposing read 32 lanes (256 bytes): the piece
+//    writes' 8 lanes (4 consecutive rows, both column halves: chunks q ^ s
+//    and (q + 4) ^ s) need s mod 4 distinct over 4 consecutive rows, and
+//    the transposing reads (rows n, n + 2 of one parity, one aligned quad of
+//    chunks each) need bit 2 of s to differ between them; both then hit
+//    distinct banks (an LDS probe counted no conflicts for either, where
+//    the former swizzle 4 ((n >> 1) & 1) + ((n >> 1) & 3) gave the writes
+//    about 8 conflict cycles each).  swz does not change under n + 4, so a
+//    sub-step's rows 8 kk further are an immediate offset.
 constexpr int kBwdBM = 256, kBwdBN = 256, kBwdThreads = 512;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-__device__ __forceinline__ int wd_swz(int n) { return (((n >> 1) & 1) << 2) | ((n >> 1) & 3); }
+__device__ __forceinline__ int wd_swz(int n) { return (n & 3) | (((n >> 1) & 1) << 2); }
 
 // raw buffer over [base, base + bytes) (bytes < 2^31): loads at offsets past
 // the range return zeros
@@ -1722,8 +1728,8 @@ k_grouped_mm_bwd(const uint8_t* __restrict__ g, const uint8_t* __restrict__ pack
   };
   // transposing-read addresses: group gq = lane / 16 -> h = gq / 2, column
   // half gq % 2; source lane s = lane % 16 -> row a = s / 4, columns 4 (s % 4).
-  // Rows tr_row + 8 kk + 4 u: the swizzle depends on u only, so sub-step kk
-  // is the immediate offset 1024 kk.
+  // Rows tr_row + 8 kk + 4 u share the swizzle of tr_row, so sub-step kk is
+  // the immediate offset 1024 kk.
   const int gq = lane >> 4, sl = lane & 15;
   const int tr_row = 32 * (gq >> 1) + (sl >> 2);
   const int tr_col = 16 * (gq & 1) + 4 * (sl & 3);
