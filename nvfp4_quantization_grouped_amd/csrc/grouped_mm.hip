@@ -715,18 +715,29 @@ struct FlSmem {
   uint8_t s8[2][kFlBN * 16];           // E8M0 scales: 16 bytes (8 steps) per column
 };
 
+// Logical workgroup id.  The dispatcher hands linear id i to XCD i % 8 (round
+// robin).  xr > 0 (a grid of exactly 8 xr workgroups, all resident at once)
+// gives XCD x the logical ids x xr .. x xr + xr - 1: whole row tiles with all
+// their column tiles, so each activation row tile is fetched into one XCD's
+// L2 and each L2 holds the weights of about one expert, instead of every L2
+// streaming all activations for its one column tile.  xr == 0: the linear id.
+__device__ __forceinline__ int xcd_major_id(int xr) {
+  return xr > 0 ? (int)(blockIdx.x & 7) * xr + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
+}
+
 // (the body is a device function template called by one kernel per tile
 // height: clang emitted no host launch stub for it as a kernel template)
 template <int BM>
 __device__ __forceinline__ void fwd_fl_body(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
                                             const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs,
                                             int experts, int64_t tokens, int64_t ndim, int64_t kdim,
-                                            uint8_t* __restrict__ out, int gx) {
+                                            uint8_t* __restrict__ out, int gx, int xr) {
   constexpr int BN = kFlBN, MT = BM / 32, NT = 2, QA = BM / 32, kThreads = kFlThreads;   // QA: activation blocks per wave
-  const int64_t col0 = (int64_t)(blockIdx.x % gx) * BN;
+  const int bid = xcd_major_id(xr);
+  const int64_t col0 = (int64_t)(bid % gx) * BN;
   TileTable<BM> tt;
   tt.build(offs, experts, tokens);
-  const TileInfo ti = tt.lookup((int)(blockIdx.x / gx));
+  const TileInfo ti = tt.lookup(bid / gx);
   if (ti.expert == -2) return;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, r = lane & 31;
@@ -903,12 +914,13 @@ template <int BM>
 __device__ __forceinline__ void fwd_fl3_body(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
                                             const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs,
                                             int experts, int64_t tokens, int64_t ndim, int64_t kdim,
-                                            uint8_t* __restrict__ out, int gx) {
+                                            uint8_t* __restrict__ out, int gx, int xr) {
   constexpr int BN = kFlBN, MT = BM / 32, NT = 2, QA = BM / 32, kThreads = kFlThreads;   // QA: activation blocks per wave
-  const int64_t col0 = (int64_t)(blockIdx.x % gx) * BN;
+  const int bid = xcd_major_id(xr);
+  const int64_t col0 = (int64_t)(bid % gx) * BN;
   TileTable<BM> tt;
   tt.build(offs, experts, tokens);
-  const TileInfo ti = tt.lookup((int)(blockIdx.x / gx));
+  const TileInfo ti = tt.lookup(bid / gx);
   if (ti.expert == -2) return;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, r = lane & 31;
@@ -1079,14 +1091,14 @@ __device__ __forceinline__ void fwd_fl3_body(const uint8_t* __restrict__ a, cons
 __global__ void __launch_bounds__(kFlThreads, 2)
 k_grouped_mm_fwd_fl128(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
                        const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
-                       int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out, int gx) {
-  fwd_fl_body<128>(a, packed, scales, offs, experts, tokens, ndim, kdim, out, gx);
+                       int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out, int gx, int xr) {
+  fwd_fl_body<128>(a, packed, scales, offs, experts, tokens, ndim, kdim, out, gx, xr);
 }
 __global__ void __launch_bounds__(kFlThreads, 2)
 k_grouped_mm_fwd_fl96(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
                       const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
-                      int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out, int gx) {
-  fwd_fl3_body<96>(a, packed, scales, offs, experts, tokens, ndim, kdim, out, gx);
+                      int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out, int gx, int xr) {
+  fwd_fl3_body<96>(a, packed, scales, offs, experts, tokens, ndim, kdim, out, gx, xr);
 }
 
 // ------------------------------------------------------ forward, W4A4
@@ -1870,9 +1882,12 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
                      (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim,      \
                      (uint8_t*)out, (int)gx)
 #define MXQ_FL_LAUNCH(BM, NWG)                                                                                   \
-  hipLaunchKernelGGL(k_grouped_mm_fwd_fl##BM, dim3((unsigned)(NWG)), dim3(kFlThreads), 0, st, (const uint8_t*)a,      \
-                     (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim, (uint8_t*)out,       \
-                     (int)gx)
+  do {                                                                                                             \
+    const int64_t xr_ = (NWG) <= slots ? ((NWG) + 7) / 8 : 0;                                                      \
+    hipLaunchKernelGGL(k_grouped_mm_fwd_fl##BM, dim3((unsigned)(xr_ ? 8 * xr_ : (NWG))), dim3(kFlThreads), 0, st,     \
+                       (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim, \
+                       (uint8_t*)out, (int)gx, (int)xr_);                                                          \
+  } while (0)
       // whole weight lines (4 steps per fetch) whenever whole generations and
       // 16-byte scale chunks exist: 3-5% faster on the routed-expert
       // projections and ~15% on the 8-expert forward than the per-step form
