@@ -156,7 +156,56 @@ struct TileTable {
     if (z < tokens) return TileInfo{z, tokens, -1};
     return TileInfo{0, 0, -2};
   }
+  // The same tiles in another slot order, for a grid that runs in one round
+  // with at most two workgroups per CU: the dispatcher places linear ids 0 ..
+  // CUs-1 one per CU and id CUs + j on id j's CU, so tiles are ordered by
+  // descending count of 32-row blocks (the whole tiles and the segment tails
+  // of BM/32 blocks first, then the tails of fewer blocks), experts ascending
+  // within a count: the short tails come last and share CUs with whole
+  // tiles.  The zero-fill slots follow as in lookup().  At most 64 experts
+  // (more take lookup()'s order).
+  __device__ __forceinline__ TileInfo lookup_by_height(int slot) const {
+    if (experts > 64) return lookup_chunked(slot);
+    constexpr int MB = BM / 32;
+    int start = __shfl_up(end, 1);
+    if ((threadIdx.x & 63) == 0) start = 0;
+    const int rows = end - start;   // 0 on lanes past the experts
+    const int nfull = rows / BM, tb = (rows % BM + 31) / 32;
+    int s = slot;
+#pragma unroll
+    for (int b = MB; b >= 1; --b) {
+      const int c = (b == MB ? nfull : 0) + (tb == b ? 1 : 0);
+      const int inc = wave_scan<false>(c);
+      const int tot = __builtin_amdgcn_readlane(inc, 63);
+      if (s < tot) {
+        const int e = __builtin_ctzll(__ballot(inc > s));
+        const int k = s - __builtin_amdgcn_readlane(inc - c, e);   // tile k of expert e in this count
+        const int64_t row0 = __builtin_amdgcn_readlane(start, e) +
+                             (int64_t)(b == MB ? k : __builtin_amdgcn_readlane(nfull, e)) * BM;
+        return TileInfo{row0, __builtin_amdgcn_readlane(end, e), e};
+      }
+      s -= tot;
+    }
+    const int64_t z = __builtin_amdgcn_readlane(end, 63) + (int64_t)s * BM;
+    if (z < tokens) return TileInfo{z, tokens, -1};
+    return TileInfo{0, 0, -2};
+  }
 };
+
+// Rows no expert owns (a zero-fill slot of the tile table) are written as
+// zeros: the BM x BN tile at (row0, col0), rows below row_end, columns below
+// ndim, by every thread of the workgroup.
+template <int BM, int BN>
+__device__ __forceinline__ void zero_tile(const TileInfo& ti, int64_t col0, uint8_t* __restrict__ out, int64_t ndim) {
+  for (int i = threadIdx.x; i < BM * BN / 8; i += blockDim.x) {
+    const int rr = i / (BN / 8), c = (i % (BN / 8)) * 8;
+    const int64_t gr = ti.row0 + rr, gc = col0 + c;
+    if (gr < ti.row_end && gc < ndim) {
+      unsigned short* dst = reinterpret_cast<unsigned short*>(out + (gr * ndim + gc) * 2);
+      for (int q = 0; q < 8 && gc + q < ndim; ++q) dst[q] = 0;
+    }
+  }
+}
 
 __device__ __forceinline__ const uint8_t* packed_e_of(const uint8_t* packed, int e, int64_t ndim, int64_t kdim) {
   return packed + (int64_t)e * ndim * (kdim / 2);
@@ -530,7 +579,6 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
   using Smem = DmaSmem<BM, W, STAGES, SCH>;
   constexpr int BN = Smem::kCols, MT = BM / 32, NT = 2, QA = Smem::kABlocksPerWave;
   constexpr int kOps = QA + 2 + (SCH == 2 ? 1 : 0);   // per wave and step (plus 1 every 8 steps when SCH == 8)
-  constexpr int kThreads = W * 64;
   // one-dimensional grid: workgroup b takes column tile b % gx of row slot b / gx
   const int64_t col0 = (int64_t)(blockIdx.x % gx) * BN;
   TileTable<BM> tt;
@@ -542,14 +590,7 @@ k_grouped_mm_fwd_dma(const uint8_t* __restrict__ a, const uint8_t* __restrict__ 
   const int h = lane >> 5, r = lane & 31;
 
   if (ti.expert == -1) {
-    for (int i = threadIdx.x; i < BM * BN / 8; i += kThreads) {
-      const int rr = i / (BN / 8), c = (i % (BN / 8)) * 8;
-      const int64_t gr = ti.row0 + rr, gc = col0 + c;
-      if (gr < ti.row_end && gc < ndim) {
-        unsigned short* dst = reinterpret_cast<unsigned short*>(out + (gr * ndim + gc) * 2);
-        for (int q = 0; q < 8 && gc + q < ndim; ++q) dst[q] = 0;
-      }
-    }
+    zero_tile<BM, BN>(ti, col0, out, ndim);
     return;
   }
 
@@ -715,46 +756,22 @@ struct FlSmem {
   uint8_t s8[2][kFlBN * 16];           // E8M0 scales: 16 bytes (8 steps) per column
 };
 
-// Logical workgroup id.  The dispatcher hands linear id i to XCD i % 8 (round
-// robin).  xr > 0 (a grid of exactly 8 xr workgroups, all resident at once)
-// gives XCD x the logical ids x xr .. x xr + xr - 1: whole row tiles with all
-// their column tiles, so each activation row tile is fetched into one XCD's
-// L2 and each L2 holds the weights of about one expert, instead of every L2
-// streaming all activations for its one column tile.  xr == 0: the linear id.
-__device__ __forceinline__ int xcd_major_id(int xr) {
-  return xr > 0 ? (int)(blockIdx.x & 7) * xr + (int)(blockIdx.x >> 3) : (int)blockIdx.x;
-}
-
 // (the body is a device function template called by one kernel per tile
 // height: clang emitted no host launch stub for it as a kernel template)
-template <int BM>
+// MTA: the tile's 32-row blocks that hold rows of its expert (1 .. BM/32);
+// the blocks past them take no activation transfers, fragment reads or MFMAs.
+// Wave `wave` adds the whole reduction for its 64 columns into acc, through
+// the LDS block sm; the caller stores acc.
+template <int BM, int MTA>
 __device__ __forceinline__ void fwd_fl_body(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
-                                            const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs,
-                                            int experts, int64_t tokens, int64_t ndim, int64_t kdim,
-                                            uint8_t* __restrict__ out, int gx, int xr) {
-  constexpr int BN = kFlBN, MT = BM / 32, NT = 2, QA = BM / 32, kThreads = kFlThreads;   // QA: activation blocks per wave
-  const int bid = xcd_major_id(xr);
-  const int64_t col0 = (int64_t)(bid % gx) * BN;
-  TileTable<BM> tt;
-  tt.build(offs, experts, tokens);
-  const TileInfo ti = tt.lookup(bid / gx);
-  if (ti.expert == -2) return;
-  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+                                            const uint8_t* __restrict__ scales, int64_t ndim, int64_t kdim,
+                                            const TileInfo ti, const int64_t col0, FlSmem<BM>& sm,
+                                            const int wave, f32x16_t (&acc)[BM / 32][2]) {
+  constexpr int MT = BM / 32, NT = 2, QA = BM / 32;   // QA: activation blocks per wave
+  static_assert(MTA >= 1 && MTA <= MT && QA == 4, "active row blocks; wave w fills row block w");
+  const int lane = threadIdx.x & 63;
   const int h = lane >> 5, r = lane & 31;
 
-  if (ti.expert == -1) {
-    for (int i = threadIdx.x; i < BM * BN / 8; i += kThreads) {
-      const int rr = i / (BN / 8), c = (i % (BN / 8)) * 8;
-      const int64_t gr = ti.row0 + rr, gc = col0 + c;
-      if (gr < ti.row_end && gc < ndim) {
-        unsigned short* dst = reinterpret_cast<unsigned short*>(out + (gr * ndim + gc) * 2);
-        for (int q = 0; q < 8 && gc + q < ndim; ++q) dst[q] = 0;
-      }
-    }
-    return;
-  }
-
-  __shared__ __attribute__((aligned(1024))) FlSmem<BM> sm;
 
   // activations: wave w fills blocks QA w .. QA w + QA - 1 of 8 rows (as in the DMA forward)
   const int64_t prow = kdim / 2, srow = kdim / 32;
@@ -780,6 +797,7 @@ __device__ __forceinline__ void fwd_fl_body(const uint8_t* __restrict__ a, const
   const uint32_t s_off = (uint32_t)(lane * srow);
 
   auto issue_a = [&](int step) {
+    if (MTA < MT && wave >= MTA) return;
 #pragma unroll
     for (int q = 0; q < QA; ++q)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_void_t*)(sm.a[step & 1] + 1024 * (QA * wave + q)), 16,
@@ -796,12 +814,6 @@ __device__ __forceinline__ void fwd_fl_body(const uint8_t* __restrict__ a, const
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_s, (lds_void_t*)(sm.s8[chunk & 1] + 1024 * wave), 16, s_off,
                                              16 * chunk, 0, 0);
   };
-
-  f32x16_t acc[MT][NT];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NT; ++j) acc[i][j] = f32x16_t{};
 
   const int nsteps = (int)(kdim / kBK), last = nsteps - 1;   // a multiple of 8
   const int ngen = nsteps >> 2, nchunk = nsteps >> 3;
@@ -862,11 +874,11 @@ __device__ __forceinline__ void fwd_fl_body(const uint8_t* __restrict__ a, const
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int off = 16 * ((4 * h + kk) ^ ((r >> 1) & 7));   // rows 32i + r share the swizzle
-      bf16x8_t fa[MT];
+      bf16x8_t fa[MTA];
 #pragma unroll
-      for (int i = 0; i < MT; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(la + i * 32 * 128 + off);
+      for (int i = 0; i < MTA; ++i) fa[i] = *reinterpret_cast<const bf16x8_t*>(la + i * 32 * 128 + off);
 #pragma unroll
-      for (int i = 0; i < MT; ++i)
+      for (int i = 0; i < MTA; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j][kk], fa[i], acc[i][j], 0, 0, 0);
@@ -890,11 +902,7 @@ __device__ __forceinline__ void fwd_fl_body(const uint8_t* __restrict__ a, const
     step(s + 2, 2);
     step(s + 3, 3);
   }
-  // nothing is pending after the last step's wait; once every wave is here the LDS is free
-  __syncthreads();
-  static_assert(sizeof(FlSmem<BM>) >= (size_t)4 * BM * 128, "epilogue block fits");
-  store_block_lds<MT>(reinterpret_cast<uint8_t*>(&sm) + wave * BM * 128, acc, lane, out, ndim, ti.row0, ti.row_end,
-                      col0 + 64 * wave, ndim);
+  // nothing is pending after the last step's wait
 }
 
 // The 96-row form with a three-slot activation ring (76 KB: still two
@@ -914,26 +922,18 @@ template <int BM>
 __device__ __forceinline__ void fwd_fl3_body(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
                                             const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs,
                                             int experts, int64_t tokens, int64_t ndim, int64_t kdim,
-                                            uint8_t* __restrict__ out, int gx, int xr) {
-  constexpr int BN = kFlBN, MT = BM / 32, NT = 2, QA = BM / 32, kThreads = kFlThreads;   // QA: activation blocks per wave
-  const int bid = xcd_major_id(xr);
-  const int64_t col0 = (int64_t)(bid % gx) * BN;
+                                            uint8_t* __restrict__ out, int gx) {
+  constexpr int BN = kFlBN, MT = BM / 32, NT = 2, QA = BM / 32;   // QA: activation blocks per wave
+  const int64_t col0 = (int64_t)(blockIdx.x % gx) * BN;
   TileTable<BM> tt;
   tt.build(offs, experts, tokens);
-  const TileInfo ti = tt.lookup(bid / gx);
+  const TileInfo ti = tt.lookup((int)(blockIdx.x / gx));
   if (ti.expert == -2) return;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, r = lane & 31;
 
   if (ti.expert == -1) {
-    for (int i = threadIdx.x; i < BM * BN / 8; i += kThreads) {
-      const int rr = i / (BN / 8), c = (i % (BN / 8)) * 8;
-      const int64_t gr = ti.row0 + rr, gc = col0 + c;
-      if (gr < ti.row_end && gc < ndim) {
-        unsigned short* dst = reinterpret_cast<unsigned short*>(out + (gr * ndim + gc) * 2);
-        for (int q = 0; q < 8 && gc + q < ndim; ++q) dst[q] = 0;
-      }
-    }
+    zero_tile<BM, BN>(ti, col0, out, ndim);
     return;
   }
 
@@ -1088,17 +1088,50 @@ __device__ __forceinline__ void fwd_fl3_body(const uint8_t* __restrict__ a, cons
                       col0 + 64 * wave, ndim);
 }
 
+// The 128-row whole-line forward.  by_height != 0 takes the slots in height
+// order (TileTable::lookup_by_height), for a grid that runs in one round:
+// on the 8-expert forward (288 tiles, 256 of full height) every CU then runs
+// one full tile and the 32 one-block tails share CUs with the first 32.
 __global__ void __launch_bounds__(kFlThreads, 2)
 k_grouped_mm_fwd_fl128(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
                        const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
-                       int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out, int gx, int xr) {
-  fwd_fl_body<128>(a, packed, scales, offs, experts, tokens, ndim, kdim, out, gx, xr);
+                       int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out, int gx,
+                       int by_height) {
+  constexpr int BM = 128, BN = kFlBN;
+  const int64_t col0 = (int64_t)(blockIdx.x % gx) * BN;
+  TileTable<BM> tt;
+  tt.build(offs, experts, tokens);
+  const int slot = (int)(blockIdx.x / gx);
+  const TileInfo ti = by_height ? tt.lookup_by_height(slot) : tt.lookup(slot);
+  if (ti.expert == -2) return;
+  if (ti.expert == -1) {
+    zero_tile<BM, BN>(ti, col0, out, ndim);
+    return;
+  }
+  // one LDS block for every instantiation below
+  __shared__ __attribute__((aligned(1024))) FlSmem<BM> sm;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  f32x16_t acc[BM / 32][2];
+#pragma unroll
+  for (int i = 0; i < BM / 32; ++i) acc[i][0] = acc[i][1] = f32x16_t{};
+  // a segment tail of fewer than BM rows runs only the 32-row blocks it fills
+  switch ((int)((min(ti.row_end - ti.row0, (int64_t)BM) + 31) / 32)) {
+    case 1: fwd_fl_body<BM, 1>(a, packed, scales, ndim, kdim, ti, col0, sm, wave, acc); break;
+    case 2: fwd_fl_body<BM, 2>(a, packed, scales, ndim, kdim, ti, col0, sm, wave, acc); break;
+    case 3: fwd_fl_body<BM, 3>(a, packed, scales, ndim, kdim, ti, col0, sm, wave, acc); break;
+    default: fwd_fl_body<BM, 4>(a, packed, scales, ndim, kdim, ti, col0, sm, wave, acc); break;
+  }
+  // once every wave is here the LDS is free
+  __syncthreads();
+  static_assert(sizeof(FlSmem<BM>) >= (size_t)4 * BM * 128, "epilogue block fits");
+  store_block_lds<BM / 32>(reinterpret_cast<uint8_t*>(&sm) + wave * BM * 128, acc, threadIdx.x & 63, out, ndim,
+                           ti.row0, ti.row_end, col0 + 64 * wave, ndim);
 }
 __global__ void __launch_bounds__(kFlThreads, 2)
 k_grouped_mm_fwd_fl96(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
                       const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
-                      int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out, int gx, int xr) {
-  fwd_fl3_body<96>(a, packed, scales, offs, experts, tokens, ndim, kdim, out, gx, xr);
+                      int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out, int gx) {
+  fwd_fl3_body<96>(a, packed, scales, offs, experts, tokens, ndim, kdim, out, gx);
 }
 
 // ------------------------------------------------------ forward, W4A4
@@ -1170,7 +1203,7 @@ __device__ __forceinline__ void w4a4_body(const uint8_t* __restrict__ xq, const 
                                           const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
                                           const int32_t* __restrict__ offs, int experts, int64_t tokens, int64_t ndim,
                                           int64_t kdim, uint8_t* __restrict__ out, int gx) {
-  constexpr int BN = kW4BN, MT = BM / 32, NT = 2, QA = BM / 32, kThreads = kW4Threads;
+  constexpr int BN = kW4BN, MT = BM / 32, NT = 2, QA = BM / 32;
   const int64_t col0 = (int64_t)(blockIdx.x % gx) * BN;
   TileTable<BM> tt;
   tt.build(offs, experts, tokens);
@@ -1180,14 +1213,7 @@ __device__ __forceinline__ void w4a4_body(const uint8_t* __restrict__ xq, const 
   const int h = lane >> 5, r = lane & 31;
 
   if (ti.expert == -1) {
-    for (int i = threadIdx.x; i < BM * BN / 8; i += kThreads) {
-      const int rr = i / (BN / 8), c = (i % (BN / 8)) * 8;
-      const int64_t gr = ti.row0 + rr, gc = col0 + c;
-      if (gr < ti.row_end && gc < ndim) {
-        unsigned short* dst = reinterpret_cast<unsigned short*>(out + (gr * ndim + gc) * 2);
-        for (int q = 0; q < 8 && gc + q < ndim; ++q) dst[q] = 0;
-      }
-    }
+    zero_tile<BM, BN>(ti, col0, out, ndim);
     return;
   }
 
@@ -1403,7 +1429,7 @@ k_grouped_mm_fwd_w4a8(const uint8_t* __restrict__ xq, const uint8_t* __restrict_
                       const uint8_t* __restrict__ packed, const uint8_t* __restrict__ scales,
                       const int32_t* __restrict__ offs, int experts, int64_t tokens, int64_t ndim, int64_t kdim,
                       uint8_t* __restrict__ out, int gx) {
-  constexpr int BM = kW8BM, BN = kW8BN, MT = BM / 32, NT = 2, QA = BM / 32, kThreads = kW8Threads;
+  constexpr int BM = kW8BM, BN = kW8BN, MT = BM / 32, NT = 2, QA = BM / 32;
   const int64_t col0 = (int64_t)(blockIdx.x % gx) * BN;
   TileTable<BM> tt;
   tt.build(offs, experts, tokens);
@@ -1413,14 +1439,7 @@ k_grouped_mm_fwd_w4a8(const uint8_t* __restrict__ xq, const uint8_t* __restrict_
   const int h = lane >> 5, r = lane & 31;
 
   if (ti.expert == -1) {
-    for (int i = threadIdx.x; i < BM * BN / 8; i += kThreads) {
-      const int rr = i / (BN / 8), c = (i % (BN / 8)) * 8;
-      const int64_t gr = ti.row0 + rr, gc = col0 + c;
-      if (gr < ti.row_end && gc < ndim) {
-        unsigned short* dst = reinterpret_cast<unsigned short*>(out + (gr * ndim + gc) * 2);
-        for (int q = 0; q < 8 && gc + q < ndim; ++q) dst[q] = 0;
-      }
-    }
+    zero_tile<BM, BN>(ti, col0, out, ndim);
     return;
   }
 
@@ -1881,19 +1900,20 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
   hipLaunchKernelGGL((k_grouped_mm_fwd_dma<BM, 4, 3, 2, SCH, true>), dim3((unsigned)(NWG)), dim3(kGemmThreads), 0, st, \
                      (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim,      \
                      (uint8_t*)out, (int)gx)
-#define MXQ_FL_LAUNCH(BM, NWG)                                                                                   \
-  do {                                                                                                             \
-    const int64_t xr_ = (NWG) <= slots ? ((NWG) + 7) / 8 : 0;                                                      \
-    hipLaunchKernelGGL(k_grouped_mm_fwd_fl##BM, dim3((unsigned)(xr_ ? 8 * xr_ : (NWG))), dim3(kFlThreads), 0, st,     \
-                       (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim, \
-                       (uint8_t*)out, (int)gx, (int)xr_);                                                          \
-  } while (0)
+#define MXQ_FL_LAUNCH(BM, NWG, ...)                                                                              \
+  hipLaunchKernelGGL(k_grouped_mm_fwd_fl##BM, dim3((unsigned)(NWG)), dim3(kFlThreads), 0, st, (const uint8_t*)a,      \
+                     (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim, (uint8_t*)out,       \
+                     (int)gx, ##__VA_ARGS__)
       // whole weight lines (4 steps per fetch) whenever whole generations and
       // 16-byte scale chunks exist: 3-5% faster on the routed-expert
       // projections and ~15% on the 8-expert forward than the per-step form
       if (sch8) {
-        if (bm96) MXQ_FL_LAUNCH(96, n96);
-        else MXQ_FL_LAUNCH(128, n128);
+        // a grid of 128-row tiles that fits in one round takes them in height
+        // order: every CU gets one tile of full height first and the short
+        // segment tails double up
+        if (n128 <= slots) MXQ_FL_LAUNCH(128, n128, 1);
+        else if (bm96) MXQ_FL_LAUNCH(96, n96);
+        else MXQ_FL_LAUNCH(128, n128, 0);
       } else if (bm96) {
         MXQ_FWD_LAUNCH(96, 2, n96);
       } else {
