@@ -206,7 +206,7 @@ def main():
             j = i % R8
             check(L.mxfp4_grouped_mm_fwd(e8_x[j].data_ptr(), 4096, 4096, e8_p[j].data_ptr(), e8_s[j].data_ptr(), 8,
                                          2048, e8_o.data_ptr(), e8_y[j].data_ptr(), sp), "e8 fwd")
-        legs.append(Leg("e8.fwd", "k_grouped_mm_fwd_fl96", "flop", 2.0 * 4096 * 2048 * 4096, e8_fn, reps=R8))
+        legs.append(Leg("e8.fwd", "k_grouped_mm_fwd_fl128_by_height", "flop", 2.0 * 4096 * 2048 * 4096, e8_fn, reps=R8))
 
     # ---------------- KV cache quantize_cache x3 + STE: 32 calls per step over 16 rotating sets of
     # 32 MiB in + 32 MiB out (537 MB of inputs per leg, twice the Infinity Cache), separate inputs per

@@ -1088,21 +1088,29 @@ __device__ __forceinline__ void fwd_fl3_body(const uint8_t* __restrict__ a, cons
                       col0 + 64 * wave, ndim);
 }
 
-// The 128-row whole-line forward.  by_height != 0 takes the slots in height
+// The 128-row whole-line forward.  BY_HEIGHT takes the slots in height
 // order (TileTable::lookup_by_height), for a grid that runs in one round:
 // on the 8-expert forward (288 tiles, 256 of full height) every CU then runs
 // one full tile and the 32 one-block tails share CUs with the first 32.
-__global__ void __launch_bounds__(kFlThreads, 2)
-k_grouped_mm_fwd_fl128(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
-                       const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
-                       int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out, int gx,
-                       int by_height) {
+// xr > 0 (one round, 8 xr CUs): the first 8 xr workgroups, one per CU, are
+// taken XCD-major -- the dispatcher puts linear id i on XCD i % 8, which
+// then runs logical ids (i % 8) xr .. (i % 8) xr + xr - 1, whole row tiles
+// with all their column tiles, so each L2 fetches about one expert's
+// weights and its share of the activations instead of every activation row
+// for one column tile; the ids past them keep their places (and CU pairs).
+template <bool BY_HEIGHT>
+__device__ __forceinline__ void fwd_fl128(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
+                                          const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs,
+                                          int experts, int64_t tokens, int64_t ndim, int64_t kdim,
+                                          uint8_t* __restrict__ out, int gx, int xr) {
   constexpr int BM = 128, BN = kFlBN;
-  const int64_t col0 = (int64_t)(blockIdx.x % gx) * BN;
+  const int bid = (xr > 0 && (int)blockIdx.x < 8 * xr) ? (int)(blockIdx.x & 7) * xr + (int)(blockIdx.x >> 3)
+                                                        : (int)blockIdx.x;
+  const int64_t col0 = (int64_t)(bid % gx) * BN;
   TileTable<BM> tt;
   tt.build(offs, experts, tokens);
-  const int slot = (int)(blockIdx.x / gx);
-  const TileInfo ti = by_height ? tt.lookup_by_height(slot) : tt.lookup(slot);
+  const int slot = bid / gx;
+  const TileInfo ti = BY_HEIGHT ? tt.lookup_by_height(slot) : tt.lookup(slot);
   if (ti.expert == -2) return;
   if (ti.expert == -1) {
     zero_tile<BM, BN>(ti, col0, out, ndim);
@@ -1126,6 +1134,19 @@ k_grouped_mm_fwd_fl128(const uint8_t* __restrict__ a, const uint8_t* __restrict_
   static_assert(sizeof(FlSmem<BM>) >= (size_t)4 * BM * 128, "epilogue block fits");
   store_block_lds<BM / 32>(reinterpret_cast<uint8_t*>(&sm) + wave * BM * 128, acc, threadIdx.x & 63, out, ndim,
                            ti.row0, ti.row_end, col0 + 64 * wave, ndim);
+}
+__global__ void __launch_bounds__(kFlThreads, 2)
+k_grouped_mm_fwd_fl128(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
+                       const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
+                       int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out, int gx) {
+  fwd_fl128<false>(a, packed, scales, offs, experts, tokens, ndim, kdim, out, gx, 0);
+}
+__global__ void __launch_bounds__(kFlThreads, 2)
+k_grouped_mm_fwd_fl128_by_height(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
+                                 const uint8_t* __restrict__ scales, const int32_t* __restrict__ offs, int experts,
+                                 int64_t tokens, int64_t ndim, int64_t kdim, uint8_t* __restrict__ out, int gx,
+                                 int xr) {
+  fwd_fl128<true>(a, packed, scales, offs, experts, tokens, ndim, kdim, out, gx, xr);
 }
 __global__ void __launch_bounds__(kFlThreads, 2)
 k_grouped_mm_fwd_fl96(const uint8_t* __restrict__ a, const uint8_t* __restrict__ packed,
@@ -1900,10 +1921,10 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
   hipLaunchKernelGGL((k_grouped_mm_fwd_dma<BM, 4, 3, 2, SCH, true>), dim3((unsigned)(NWG)), dim3(kGemmThreads), 0, st, \
                      (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim,      \
                      (uint8_t*)out, (int)gx)
-#define MXQ_FL_LAUNCH(BM, NWG, ...)                                                                              \
-  hipLaunchKernelGGL(k_grouped_mm_fwd_fl##BM, dim3((unsigned)(NWG)), dim3(kFlThreads), 0, st, (const uint8_t*)a,      \
+#define MXQ_FL_LAUNCH(KERNEL, NWG)                                                                               \
+  hipLaunchKernelGGL(KERNEL, dim3((unsigned)(NWG)), dim3(kFlThreads), 0, st, (const uint8_t*)a,                       \
                      (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim, wk_dim, (uint8_t*)out,       \
-                     (int)gx, ##__VA_ARGS__)
+                     (int)gx)
       // whole weight lines (4 steps per fetch) whenever whole generations and
       // 16-byte scale chunks exist: 3-5% faster on the routed-expert
       // projections and ~15% on the 8-expert forward than the per-step form
@@ -1911,9 +1932,14 @@ hipError_t launch_grouped_mm(bool bwd, const void* a, int64_t tokens, const int8
         // a grid of 128-row tiles that fits in one round takes them in height
         // order: every CU gets one tile of full height first and the short
         // segment tails double up
-        if (n128 <= slots) MXQ_FL_LAUNCH(128, n128, 1);
-        else if (bm96) MXQ_FL_LAUNCH(96, n96);
-        else MXQ_FL_LAUNCH(128, n128, 0);
+        if (n128 <= slots) {
+          const int xr = cus > 0 && cus % 8 == 0 && n128 >= cus ? cus / 8 : 0;
+          hipLaunchKernelGGL(k_grouped_mm_fwd_fl128_by_height, dim3((unsigned)n128), dim3(kFlThreads), 0, st,
+                             (const uint8_t*)a, (const uint8_t*)packed, scales, offs, (int)experts, tokens, wn_dim,
+                             wk_dim, (uint8_t*)out, (int)gx, xr);
+        }
+        else if (bm96) MXQ_FL_LAUNCH(k_grouped_mm_fwd_fl96, n96);   // (several rounds)
+        else MXQ_FL_LAUNCH(k_grouped_mm_fwd_fl128, n128);
       } else if (bm96) {
         MXQ_FWD_LAUNCH(96, 2, n96);
       } else {
