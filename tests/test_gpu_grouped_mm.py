@@ -233,6 +233,28 @@ def test_grouped_mm_e8_workload():
     print("E=8 fwd rel Frobenius", {k: f"{v:.2e}" for k, v in errs.items()})
 
 
+def test_one_round_height_order():
+    """A forward grid of at most two workgroups per CU (328 slots of 128 x
+    256 for 20 experts) takes its tiles in height order, the first one per CU
+    XCD-major: segment tails of 1, 2, 3 and 4 row blocks, whole tiles, empty
+    experts, a one-row expert and 77 uncovered rows all match the oracle, and
+    a second call gives the same bits."""
+    counts = [128, 31, 64, 65, 96, 97, 0, 127, 1, 256, 300, 0, 33, 200, 160, 129, 190, 250, 100, 300]
+    E, N, K = len(counts), 2048, 512
+    T = sum(counts) + 77
+    offs = np.cumsum(counts).astype(np.int32)
+    assert N // 256 * ((T + 127) // 128 + E) <= 512
+    packed, scales, xb = random_case(4242, E, T, N, K, offs)
+    pt, st = gpu_weights(packed, scales)
+    ot = torch.from_numpy(offs).to(dev())
+    xg = to_gpu_bits(xb, "bf16")
+    y = mxq.mxfp4_grouped_mm_fwd(xg, pt, st, ot)
+    want = oracle.grouped_mm_fwd(oracle.from_dtype_bits(xb, "bf16"), packed, scales, offs)
+    check_segments(bf16_values(y), want, offs, what="one-round height order fwd")
+    y2 = mxq.mxfp4_grouped_mm_fwd(xg, pt, st, ot)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
 @pytest.mark.timeout(900)
 def test_moe_layer_workload_sampled_rows():
     """32 local experts, hidden 7168, intermediate 2048, 131072 routed rows
