@@ -908,7 +908,8 @@ __device__ __forceinline__ void fwd_fl_body(const uint8_t* __restrict__ a, const
 // The 96-row form with a three-slot activation ring (76 KB: still two
 // workgroups per CU; 128-row tiles would need 88 KB): activations get two
 // steps of lead and generations three, as in the W4A8 forward.  On the
-// 8-expert forward, bit-identical, 73.5 -> 72.1 us against the two-slot
+// 8-expert forward (before its height-ordered 128-row grid), bit-identical,
+// 73.5 -> 72.1 us against the two-slot
 // body.
 template <int BM>
 struct Fl3Smem {
